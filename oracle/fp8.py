@@ -1,0 +1,144 @@
+"""FP8 e4m3 pre-pass of the attention forward pass, written from its definition.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Sources (FlashAttention-3 digest, section 3.5 "FP8 adaptation"; blog article section 4):
+
+* Block quantisation: one scale per block of 64 tokens x d of each head of Q, K and V.
+  The scale is a power of two (the blog article, section 4, insists on power-of-two
+  scales that are uniform inside a block), so folding it into the scores is exact.
+* Incoherent processing: Q and K are multiplied by the same random orthogonal matrix
+  M = D H / sqrt(d) before quantising, with D a random +-1 diagonal and H the Sylvester
+  Hadamard matrix; (QM)(KM)^T = QK^T.  Here H is kept unnormalised (entries +-1), so
+  (Q D H)(K D H)^T = d * Q K^T and the 1/d is folded into K's block scales.  V is not
+  rotated.
+* e4m3 is the OCP 8-bit floating-point format E4M3 ("fn" variant): 4 exponent bits with
+  bias 7, 3 mantissa bits, subnormals, no infinities, S.1111.111 is NaN, largest finite
+  magnitude 448.  Encoding rounds to nearest with ties to even and clamps to +-448.
+
+Readings where the pages leave a step open:
+
+* Block exponent e is the smallest integer with amax <= 448 * 2**e (amax = 0 gives e = 0),
+  so the block's largest magnitude lands in [224, 448] after scaling.
+* Blocks start at token 0 of every (batch, head); a short last block is scaled over its
+  valid tokens only.
+* The Hadamard sums are formed exactly (fp64 sums of bf16 values with +-1 weights are exact
+  unless one row spans more than 2**38 in magnitude), so the code chosen for each element is
+  the round-to-nearest-even of the exact rotated value.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+BLOCK = 64
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Value of each e4m3fn code (uint8) as float64; NaN codes decode to NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+# All non-negative finite magnitudes, indexed by their code 0x00..0x7E (increasing).
+_POS_TABLE = e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """Nearest e4m3fn code to each float64 value, ties to the even code, clamped to +-448.
+
+    Implemented as a search over the table of representable magnitudes, which is the
+    format's definition rather than a bit trick.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(np.isnan(x)):
+        raise ValueError("e4m3_encode got NaN")
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    hi = np.searchsorted(_POS_TABLE, a, side="left")  # first table entry >= a
+    hi = np.minimum(hi, 0x7E)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _POS_TABLE[lo]
+    d_hi = _POS_TABLE[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a == _POS_TABLE[hi], hi, code)
+    # the sign is kept, also when the magnitude rounds to zero (IEEE-style signed zero)
+    return (code | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def hadamard(d: int) -> np.ndarray:
+    """Unnormalised Sylvester Hadamard matrix: H[i, j] = (-1)**popcount(i & j)."""
+    if d <= 0 or d & (d - 1):
+        raise ValueError("d must be a power of two")
+    i = np.arange(d)
+    pc = np.vectorize(lambda x: bin(int(x)).count("1"))(i[:, None] & i[None, :])
+    return np.where(pc % 2 == 0, 1.0, -1.0)
+
+
+def block_exponent(amax: float) -> int:
+    """Smallest integer e with amax <= 448 * 2**e; 0 for amax == 0."""
+    if amax == 0.0:
+        return 0
+    m, ex = math.frexp(amax)  # amax = m * 2**ex with 0.5 <= m < 1
+    # 448 = 0.875 * 2**9, and m / 0.875 lies in (0.57, 1.15)
+    return ex - 9 if m <= 0.875 else ex - 8
+
+
+def rotate(x: np.ndarray, signs: np.ndarray | None) -> np.ndarray:
+    """x D H along the last axis (fp64).  signs=None means no rotation."""
+    x = np.asarray(x, dtype=np.float64)
+    if signs is None:
+        return x
+    d = x.shape[-1]
+    return (x * np.asarray(signs, dtype=np.float64)) @ hadamard(d)
+
+
+def quantize_blocks(y: np.ndarray, block: int = BLOCK):
+    """Per-(batch, head, 64-token block) power-of-two scaling and e4m3 encoding.
+
+    y: [B, N, H, d] float64.  Returns (codes uint8 [B,N,H,d], exponents int [B,H,nblk]).
+    """
+    B, N, H, d = y.shape
+    nblk = -(-N // block)
+    codes = np.empty(y.shape, dtype=np.uint8)
+    exps = np.zeros((B, H, nblk), dtype=np.int64)
+    for b in range(B):
+        for h in range(H):
+            for j in range(nblk):
+                t0, t1 = j * block, min(N, (j + 1) * block)
+                blk = y[b, t0:t1, h, :]
+                e = block_exponent(float(np.max(np.abs(blk))) if blk.size else 0.0)
+                exps[b, h, j] = e
+                codes[b, t0:t1, h, :] = e4m3_encode(np.ldexp(blk, -e))
+    return codes, exps
+
+
+def fp8_prepare(q, k, v, signs: np.ndarray | None, block: int = BLOCK):
+    """The full pre-pass on fp64 copies of the bf16 inputs ([B, N, H, d] each).
+
+    Returns q8, k8, v8 (uint8 e4m3 codes) and q_scale, k_scale, v_scale (float32
+    [B, H, nblk], powers of two).  With signs given, Q and K are rotated by D H and K's
+    scales carry the extra 1/d.
+    """
+    d = np.shape(q)[-1]
+    q8, eq = quantize_blocks(rotate(q, signs), block)
+    k8, ek = quantize_blocks(rotate(k, signs), block)
+    v8, ev = quantize_blocks(np.asarray(v, dtype=np.float64), block)
+    ek_total = ek - (int(math.log2(d)) if signs is not None else 0)
+    to_scale = lambda e: np.ldexp(np.ones(e.shape, dtype=np.float32), e.astype(np.int32))
+    return q8, k8, v8, to_scale(eq), to_scale(ek_total), to_scale(ev)
+
+
+def dequantize(codes: np.ndarray, scales: np.ndarray, block: int = BLOCK) -> np.ndarray:
+    """codes [B,N,H,d] with scales [B,H,nblk] -> float64 [B,N,H,d] (exact)."""
+    B, N, H, d = codes.shape
+    tok_blk = np.arange(N) // block
+    s = np.asarray(scales, dtype=np.float64)[:, :, tok_blk]  # [B, H, N]
+    return e4m3_decode(codes) * s.transpose(0, 2, 1)[..., None]
