@@ -1,0 +1,228 @@
+"""Python binding of libattn -- the fused exact-attention forward pass for MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP kernels of
+``libattn.so`` (sources under ``csrc/``, C ABI in ``include/attn.h``).  PyTorch supplies device
+memory and streams.  There is no fallback: if the library cannot be loaded, every call raises.
+
+Entry points carry the names of the C ABI:
+
+* :func:`attn_fwd` -- O and LSE of exact attention (bf16 / fp16 / fp8-e4m3 inputs; dense or
+  packed variable-length; causal or not; grouped-query heads).
+* :func:`attn_fp8_prepare` -- Hadamard rotation + per-block power-of-two e4m3 quantisation.
+* :func:`attn_strerror` -- text of a status code.
+
+Helpers :func:`attention` and :func:`fp8_prepare` allocate the outputs and call the above.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+__all__ = ["AttnError", "attn_fwd", "attn_fp8_prepare", "attn_strerror", "attention", "fp8_prepare",
+           "load_library", "LIB_PATH", "ATTN_BF16", "ATTN_FP16", "ATTN_FP8_E4M3"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libattn.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "attn.h")
+
+ATTN_BF16, ATTN_FP16, ATTN_FP8_E4M3 = 0, 1, 2
+ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_ALIGN, ATTN_ERR_HIP = 0, -1, -2, -3, -4
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: status {status} ({attn_strerror(status)})")
+        self.status = status
+
+
+def load_library(build_if_missing: bool = True):
+    """Load libattn.so; compile it first only when no built library exists."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        if not build_if_missing:
+            raise OSError(f"{LIB_PATH} is not built")
+        from . import build as _build
+
+        _build.build()
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, P, I, I, F, I, P, P, P, P]
+    lib.attn_fwd.restype = I
+    lib.attn_fp8_prepare.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, P]
+    lib.attn_fp8_prepare.restype = I
+    lib.attn_strerror.argtypes = [I]
+    lib.attn_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/attn.h declares."""
+    text = open(HEADER).read()
+    return re.findall(r"^(?:int|const char\*)\s+(attn_\w+)\s*\(", text, flags=re.M)
+
+
+def attn_strerror(status: int) -> str:
+    return load_library().attn_strerror(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check_tensor(t, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (strided views are not supported)")
+
+
+_FP8_TYPES = tuple(x for x in (getattr(torch, "float8_e4m3fn", None), torch.uint8) if x is not None)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float16:
+        return ATTN_FP16
+    if t.dtype in _FP8_TYPES:
+        return ATTN_FP8_E4M3
+    raise TypeError(f"unsupported input dtype {t.dtype}")
+
+
+def attn_fwd(q, k, v, o, lse, *, causal: bool = False, alpha: float | None = None, cu_seqlens=None,
+             max_seqlen: int | None = None, q_scale=None, k_scale=None, v_scale=None, stream=None) -> None:
+    """Enqueue attn_fwd on ``stream`` (default: torch's current stream).
+
+    Dense: q/o [B, N, Hq, d], k/v [B, N, Hkv, d], lse [B, Hq, N].
+    Varlen: q/o [T, Hq, d], k/v [T, Hkv, d], lse [Hq, T], cu_seqlens int32 [B+1] on the GPU and
+    ``max_seqlen`` >= the longest sequence.  fp8 inputs (float8_e4m3fn or uint8 codes) need the
+    three per-block scale tensors.
+    """
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse)):
+        _check_tensor(t, name)
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    if cu_seqlens is None:
+        if q.dim() != 4:
+            raise ValueError("dense q must be [B, N, Hq, d]")
+        B, N, Hq, d = q.shape
+        Hkv = k.shape[2]
+    else:
+        _check_tensor(cu_seqlens, "cu_seqlens")
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+        if q.dim() != 3 or max_seqlen is None:
+            raise ValueError("varlen q must be [T, Hq, d] and max_seqlen must be given")
+        B = cu_seqlens.numel() - 1
+        N = int(max_seqlen)
+        _, Hq, d = q.shape
+        Hkv = k.shape[1]
+    kv_shape = (B, N, Hkv, d) if cu_seqlens is None else (q.shape[0], Hkv, d)
+    lse_shape = (B, Hq, N) if cu_seqlens is None else (Hq, q.shape[0])
+    if tuple(k.shape) != kv_shape or tuple(v.shape) != kv_shape:
+        raise ValueError(f"k and v must be {kv_shape}, got {tuple(k.shape)} and {tuple(v.shape)}")
+    if tuple(o.shape) != tuple(q.shape) or tuple(lse.shape) != lse_shape:
+        raise ValueError(f"o must be {tuple(q.shape)} and lse {lse_shape}")
+    dt = _dtype_code(q)
+    if _dtype_code(k) != dt or _dtype_code(v) != dt:
+        raise TypeError("q, k and v must share one dtype")
+    if dt != ATTN_FP8_E4M3:
+        q_scale = k_scale = v_scale = None
+    else:
+        nblk = -(-N // 64)
+        for name, t, H in (("q_scale", q_scale, Hq), ("k_scale", k_scale, Hkv), ("v_scale", v_scale, Hkv)):
+            if t is not None:
+                _check_tensor(t, name)
+                if t.dtype != torch.float32 or tuple(t.shape) != (B, H, nblk):
+                    raise ValueError(f"{name} must be float32 {(B, H, nblk)}")
+        if o.dtype != torch.bfloat16:
+            raise TypeError("o must be bfloat16 for fp8 inputs")
+    if dt == ATTN_FP16 and o.dtype != torch.float16 or dt == ATTN_BF16 and o.dtype != torch.bfloat16:
+        raise TypeError("o must have the dtype of q (bf16 or fp16)")
+    alpha = (1.0 / d ** 0.5) if alpha is None else float(alpha)
+    st = load_library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N,
+                                 _ptr(cu_seqlens), d, int(bool(causal)), alpha, dt,
+                                 _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), _stream_handle(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd")
+
+
+def attention(q, k, v, *, causal: bool = False, alpha: float | None = None, cu_seqlens=None,
+              max_seqlen: int | None = None, q_scale=None, k_scale=None, v_scale=None, stream=None):
+    """Allocate O (bf16, or fp16 for fp16 inputs) and LSE (fp32) and call :func:`attn_fwd`."""
+    out_dtype = torch.float16 if q.dtype == torch.float16 else torch.bfloat16
+    o = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    if cu_seqlens is None:
+        B, N, Hq, _ = q.shape
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    else:
+        T, Hq, _ = q.shape
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+    attn_fwd(q, k, v, o, lse, causal=causal, alpha=alpha, cu_seqlens=cu_seqlens, max_seqlen=max_seqlen,
+             q_scale=q_scale, k_scale=k_scale, v_scale=v_scale, stream=stream)
+    return o, lse
+
+
+def attn_fp8_prepare(q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, *, hadamard_signs=None,
+                     stream=None) -> None:
+    """Enqueue the FP8 pre-pass: bf16 q/k/v [B, N, H, d] -> e4m3 codes + fp32 block scales
+    [B, H, ceil(N/64)].  ``hadamard_signs``: int8 [d] of +-1 on the GPU, or None for no rotation."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("q8", q8), ("k8", k8), ("v8", v8),
+                    ("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
+        _check_tensor(t, name)
+    if hadamard_signs is not None:
+        _check_tensor(hadamard_signs, "hadamard_signs")
+        if hadamard_signs.dtype != torch.int8:
+            raise TypeError("hadamard_signs must be int8")
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("attn_fp8_prepare takes bf16 inputs")
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    nblk = -(-N // 64)
+    if tuple(k.shape) != (B, N, Hkv, d) or tuple(v.shape) != (B, N, Hkv, d):
+        raise ValueError("k and v must be [B, N, Hkv, d] like q")
+    for t, ref in ((q8, q), (k8, k), (v8, v)):
+        if tuple(t.shape) != tuple(ref.shape) or t.element_size() != 1:
+            raise ValueError("fp8 outputs must be 1-byte tensors shaped like their inputs")
+    for t, H in ((q_scale, Hq), (k_scale, Hkv), (v_scale, Hkv)):
+        if t.dtype != torch.float32 or tuple(t.shape) != (B, H, nblk):
+            raise ValueError(f"scales must be float32 {(B, H, nblk)}")
+    if hadamard_signs is not None and hadamard_signs.numel() != d:
+        raise ValueError("hadamard_signs must have d entries")
+    st = load_library().attn_fp8_prepare(_ptr(q), _ptr(k), _ptr(v), _ptr(q8), _ptr(k8), _ptr(v8),
+                                         _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), B, Hq, Hkv, N, d,
+                                         _ptr(hadamard_signs), _stream_handle(stream))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fp8_prepare")
+
+
+def fp8_prepare(q, k, v, *, hadamard_signs=None, stream=None):
+    """Allocate the e4m3 tensors (as uint8 codes) and scales and call :func:`attn_fp8_prepare`."""
+    B, N, Hq, d = q.shape
+    Hkv = k.shape[2]
+    nblk = -(-N // 64)
+    dev = q.device
+    q8 = torch.empty(q.shape, dtype=torch.uint8, device=dev)
+    k8 = torch.empty(k.shape, dtype=torch.uint8, device=dev)
+    v8 = torch.empty(v.shape, dtype=torch.uint8, device=dev)
+    qs = torch.empty((B, Hq, nblk), dtype=torch.float32, device=dev)
+    ks = torch.empty((B, Hkv, nblk), dtype=torch.float32, device=dev)
+    vs = torch.empty((B, Hkv, nblk), dtype=torch.float32, device=dev)
+    attn_fp8_prepare(q, k, v, q8, k8, v8, qs, ks, vs, hadamard_signs=hadamard_signs, stream=stream)
+    return q8, k8, v8, qs, ks, vs

@@ -1,0 +1,90 @@
+// api.hip -- the C ABI of libattn (declared in include/attn.h): argument validation and
+// dispatch to the kernel launchers.  Host code only.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "attn.h"
+#include "internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Largest element count any one tensor may have, so 64-bit offsets never overflow and the
+// per-row arithmetic in the kernels stays in int range.
+constexpr long long kMaxTokens = 1LL << 31;
+
+int validate_common(const void* q, const void* k, const void* v, const void* o, const void* out2,
+                    int B, int Hq, int Hkv, int N) {
+  if (!q || !k || !v || !o || !out2) return ATTN_ERR_INVALID;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0) return ATTN_ERR_INVALID;
+  if (Hq % Hkv != 0) return ATTN_ERR_INVALID;
+  if ((long long)B * N >= kMaxTokens) return ATTN_ERR_INVALID;
+  return ATTN_OK;
+}
+
+int status_of(hipError_t err) {
+  if (err == hipSuccess) return ATTN_OK;
+  if (err == hipErrorNotSupported) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_strerror(int status) {
+  switch (status) {
+    case ATTN_OK: return "success";
+    case ATTN_ERR_INVALID: return "invalid argument (null pointer, non-positive size, Hq % Hkv != 0, "
+                                  "alpha not finite and > 0, or FP8 without scales)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported combination of head dim, dtype and mode";
+    case ATTN_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+    case ATTN_ERR_HIP: return "HIP runtime refused the launch";
+    default: return "unknown status";
+  }
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+             int N, const int* cu_seqlens, int d, int causal, float alpha, attn_dtype_t dtype,
+             const float* q_scale, const float* k_scale, const float* v_scale, hipStream_t stream) {
+  int rc = validate_common(q, k, v, o, lse, B, Hq, Hkv, N);
+  if (rc != ATTN_OK) return rc;
+  if (!(isfinite(alpha) && alpha > 0.f)) return ATTN_ERR_INVALID;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_ALIGN;
+
+  attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, cu_seqlens, d, causal, alpha, q_scale, k_scale, v_scale};
+  hipError_t err;
+  switch (dtype) {
+    case ATTN_BF16:
+    case ATTN_FP16:
+      if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
+      err = attn::launch_fwd_16bit(a, dtype == ATTN_BF16, stream);
+      break;
+    case ATTN_FP8_E4M3:
+      if (!q_scale || !k_scale || !v_scale) return ATTN_ERR_INVALID;
+      if (d != 128 || cu_seqlens != nullptr || causal) return ATTN_ERR_UNSUPPORTED;
+      err = attn::launch_fwd_fp8(a, stream);
+      break;
+    default:
+      return ATTN_ERR_UNSUPPORTED;
+  }
+  return status_of(err);
+}
+
+int attn_fp8_prepare(const void* q, const void* k, const void* v, void* q8, void* k8, void* v8,
+                     float* q_scale, float* k_scale, float* v_scale, int B, int Hq, int Hkv, int N, int d,
+                     const signed char* hadamard_signs, hipStream_t stream) {
+  int rc = validate_common(q, k, v, q8, k8, B, Hq, Hkv, N);
+  if (rc != ATTN_OK) return rc;
+  if (!v8 || !q_scale || !k_scale || !v_scale) return ATTN_ERR_INVALID;
+  if (d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q8) || !aligned16(k8) || !aligned16(v8))
+    return ATTN_ERR_ALIGN;
+  attn::PrepareArgs a{q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, B, Hq, Hkv, N, d, hadamard_signs};
+  return status_of(attn::launch_fp8_prepare(a, stream));
+}
+
+}  // extern "C"

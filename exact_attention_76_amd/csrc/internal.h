@@ -1,0 +1,48 @@
+// internal.h -- launcher interface between the C-ABI layer (api.hip) and the kernel files.
+// Arguments reaching these launchers have already been validated by api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, N;          // N: sequence length (dense) or longest sequence (varlen)
+  const int* cu_seqlens;      // device int32 [B+1] or nullptr
+  int d;
+  int causal;
+  float alpha;
+  const float* q_scale;       // fp8 only
+  const float* k_scale;
+  const float* v_scale;
+};
+
+// 16-bit inputs (bf16 when is_bf16, else fp16); d in {64, 128, 256}.
+hipError_t launch_fwd_16bit(const FwdArgs& a, bool is_bf16, hipStream_t stream);
+
+// e4m3 inputs with per-block scales; d == 128, dense, non-causal.
+hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream);
+
+struct PrepareArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* q8;
+  void* k8;
+  void* v8;
+  float* q_scale;
+  float* k_scale;
+  float* v_scale;
+  int B, Hq, Hkv, N, d;
+  const signed char* signs;
+};
+
+hipError_t launch_fp8_prepare(const PrepareArgs& a, hipStream_t stream);
+
+}  // namespace attn

@@ -1,0 +1,121 @@
+/*
+ * attn.h -- C ABI of libattn, the fused exact-attention forward pass for AMD gfx950 (MI355X).
+ *
+ * What is computed (FlashAttention-3 pages; the zenmind digest "FlashAttention-3: pushing
+ * attention to Hopper's peak with asynchrony and low precision", section 3.1 for the
+ * definition and section 3.2 / Algorithm 1 for the tiled forward pass and its outputs):
+ *
+ *   for every sequence b, query head h and query i of that sequence
+ *     S_ij = alpha * <q_i, k_j>            over the visible keys j
+ *     P_ij = softmax_j(S_ij)               (row maximum subtracted before exp)
+ *     O_i  = sum_j P_ij v_j
+ *     L_i  = m_i + ln(l_i)                 (m_i = max_j S_ij, l_i = sum_j exp(S_ij - m_i))
+ *
+ * S and P never reach device memory: the kernels tile the keys and use an online softmax.
+ * Visible keys: all keys of the same sequence (non-causal) or keys j <= i (causal).
+ * Grouped-query attention: query head h reads key/value head h / (Hq / Hkv); K and V are
+ * never replicated (digest section 3.2, "MQA/GQA").
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library allocates
+ *     nothing and keeps no state between calls, so calls are thread-safe.
+ *   - Work is enqueued on `stream` (NULL = the default stream) and the call returns without
+ *     synchronising.  Faults of the enqueued kernels surface at the caller's next sync.
+ *   - Every argument is validated before anything is enqueued; a non-zero status means
+ *     nothing was launched.  attn_strerror() names a status.
+ *   - Tensors are contiguous with the head dimension innermost (d contiguous), and every
+ *     q/k/v/o pointer must be 16-byte aligned (misaligned or strided views are the silent-
+ *     wrong-result pitfall named in the blog article's deployment section, so they are
+ *     rejected instead).
+ */
+#ifndef LIBATTN_ATTN_H
+#define LIBATTN_ATTN_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q/k/v.  The output o is bf16 for ATTN_BF16 and ATTN_FP8_E4M3 inputs and
+ * fp16 for ATTN_FP16 inputs; lse is always fp32. */
+typedef enum {
+  ATTN_BF16 = 0,
+  ATTN_FP16 = 1,
+  ATTN_FP8_E4M3 = 2 /* OCP E4M3 ("fn": max 448, no infinities) with per-block scales */
+} attn_dtype_t;
+
+enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID = -1,     /* null pointer, non-positive size, Hq % Hkv != 0, bad alpha,
+                                FP8 without scales */
+  ATTN_ERR_UNSUPPORTED = -2, /* head dim / dtype / mode combination without a kernel */
+  ATTN_ERR_ALIGN = -3,       /* a tensor pointer is not 16-byte aligned */
+  ATTN_ERR_HIP = -4          /* the HIP runtime refused the launch */
+};
+
+/*
+ * attn_fwd -- O and L of exact attention, one call per batch.
+ *
+ * Dense layout (cu_seqlens == NULL):
+ *   q, o  [B, N, Hq, d]     k, v [B, N, Hkv, d]     lse [B, Hq, N]
+ * Variable-length layout (cu_seqlens != NULL; sequences packed along one token axis, the
+ * varlen interface of the guijiagi overview's "variable-length sequences" paragraph):
+ *   cu_seqlens: int32 [B + 1] on the device, cu_seqlens[0] = 0, non-decreasing; sequence b
+ *   holds tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 and T = cu_seqlens[B].
+ *   q, o  [T, Hq, d]        k, v [T, Hkv, d]        lse [Hq, T]
+ *   N must be >= the longest sequence (it sizes the grid, so no device-to-host copy is
+ *   needed); sequences longer than N are not fully processed.
+ *
+ * d:       64, 128 or 256 for ATTN_BF16 / ATTN_FP16; 128 for ATTN_FP8_E4M3.
+ * causal:  0 = every key of the sequence is visible; 1 = key j visible to query i iff j <= i.
+ * alpha:   score scale, finite and > 0 (usually 1/sqrt(d), digest section 3.1).
+ * dtype:   element type of q, k, v.
+ * q_scale, k_scale, v_scale (ATTN_FP8_E4M3 only, else ignored): fp32 device arrays of
+ *   powers of two, [B, Hq, ceil(N/64)] for q and [B, Hkv, ceil(N/64)] for k and v; block c
+ *   covers tokens 64c .. 64c+63 of a (batch, head).  The attention inputs are
+ *   e4m3(x) * scale (digest section 3.5, block quantisation).  FP8 currently requires the
+ *   dense layout and causal == 0.
+ * lse:     fp32, natural log, in units of the scaled scores S.  A row without visible keys
+ *          gets O = 0 and L = -inf.
+ *
+ * Returns ATTN_OK or a negative status; on error nothing is enqueued.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int Hq, int Hkv, int N, const int* cu_seqlens,
+             int d, int causal, float alpha, attn_dtype_t dtype,
+             const float* q_scale, const float* k_scale, const float* v_scale,
+             hipStream_t stream);
+
+/*
+ * attn_fp8_prepare -- the FP8 pre-pass (digest section 3.5: block quantisation and
+ * incoherent processing; power-of-two block scales as the blog article's FP8 section
+ * requires).
+ *
+ * Inputs q [B, N, Hq, d], k and v [B, N, Hkv, d], bf16, dense layout, d = 128.
+ * If hadamard_signs (device int8 [d], each +1 or -1) is non-NULL, q and k are first
+ * multiplied along d by D H, where D = diag(signs) and H is the unnormalised Sylvester
+ * Hadamard matrix (entries +-1); v is never rotated.  NULL skips the rotation.
+ * Then, per (batch, head, block of 64 tokens), with amax the largest magnitude in the
+ * block, e is the smallest integer with amax <= 448 * 2^e (e = 0 for an all-zero block),
+ * every element is divided by 2^e and rounded to the nearest e4m3 value (ties to even,
+ * sign kept), and the block scale 2^e is written -- times 1/d for k when rotated, so that
+ * (q8 * q_scale) . (k8 * k_scale) approximates q . k.
+ * Outputs q8/k8/v8: uint8 e4m3 codes in the input layouts; scales fp32 [B, H, ceil(N/64)].
+ * The rotated sums are formed in fp64, so each code is the rounding of the exact value.
+ */
+int attn_fp8_prepare(const void* q, const void* k, const void* v,
+                     void* q8, void* k8, void* v8,
+                     float* q_scale, float* k_scale, float* v_scale,
+                     int B, int Hq, int Hkv, int N, int d,
+                     const signed char* hadamard_signs,
+                     hipStream_t stream);
+
+/* Static description of a status code. */
+const char* attn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBATTN_ATTN_H */

@@ -1,0 +1,97 @@
+"""The C ABI of libattn on the CPU: the library loads, exports every function include/attn.h
+declares, and rejects bad arguments with the documented status before anything reaches HIP
+(the blog article's deployment pitfalls -- misaligned or strided tensors, oversize launches --
+become explicit errors).  No GPU is touched: every call here fails validation."""
+import ctypes
+import subprocess
+
+import pytest
+
+import exact_attention_76_amd as ea
+
+A = 1 << 20  # a 16-byte aligned stand-in address; never dereferenced
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ea.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = ea.header_functions()
+    assert set(names) == {"attn_fwd", "attn_fp8_prepare", "attn_strerror"}
+    out = subprocess.run(["nm", "-D", "--defined-only", ea.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for n in names:
+        assert n in exported, f"{n} not exported"
+        assert hasattr(lib, n)
+
+
+def test_strerror(lib):
+    for st in (0, -1, -2, -3, -4):
+        assert ea.attn_strerror(st) and ea.attn_strerror(st) != "unknown status"
+    assert ea.attn_strerror(7) == "unknown status"
+
+
+def fwd(lib, q=A, k=A, v=A, o=A, lse=A, B=1, Hq=2, Hkv=2, N=128, cu=None, d=128, causal=0, alpha=0.125,
+        dtype=ea.ATTN_BF16, qs=None, ks=None, vs=None):
+    P = ctypes.c_void_p
+    return lib.attn_fwd(P(q), P(k), P(v), P(o), P(lse), B, Hq, Hkv, N, P(cu) if cu else None, d, causal,
+                        alpha, dtype, P(qs) if qs else None, P(ks) if ks else None, P(vs) if vs else None,
+                        None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), ea.ATTN_ERR_INVALID),
+    (dict(k=0), ea.ATTN_ERR_INVALID),
+    (dict(v=0), ea.ATTN_ERR_INVALID),
+    (dict(o=0), ea.ATTN_ERR_INVALID),
+    (dict(lse=0), ea.ATTN_ERR_INVALID),
+    (dict(B=0), ea.ATTN_ERR_INVALID),
+    (dict(N=0), ea.ATTN_ERR_INVALID),
+    (dict(N=-5), ea.ATTN_ERR_INVALID),
+    (dict(Hq=0), ea.ATTN_ERR_INVALID),
+    (dict(Hkv=0), ea.ATTN_ERR_INVALID),
+    (dict(Hq=6, Hkv=4), ea.ATTN_ERR_INVALID),
+    (dict(alpha=0.0), ea.ATTN_ERR_INVALID),
+    (dict(alpha=-1.0), ea.ATTN_ERR_INVALID),
+    (dict(alpha=float("nan")), ea.ATTN_ERR_INVALID),
+    (dict(alpha=float("inf")), ea.ATTN_ERR_INVALID),
+    (dict(causal=2), ea.ATTN_ERR_INVALID),
+    (dict(B=1 << 16, N=1 << 15), ea.ATTN_ERR_INVALID),
+    (dict(q=A + 2), ea.ATTN_ERR_ALIGN),
+    (dict(k=A + 8), ea.ATTN_ERR_ALIGN),
+    (dict(v=A + 4), ea.ATTN_ERR_ALIGN),
+    (dict(o=A + 6), ea.ATTN_ERR_ALIGN),
+    (dict(d=96), ea.ATTN_ERR_UNSUPPORTED),
+    (dict(d=32), ea.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=7), ea.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=ea.ATTN_FP8_E4M3), ea.ATTN_ERR_INVALID),  # no scales
+    (dict(dtype=ea.ATTN_FP8_E4M3, qs=A, ks=A), ea.ATTN_ERR_INVALID),
+    (dict(dtype=ea.ATTN_FP8_E4M3, qs=A, ks=A, vs=A, d=64), ea.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=ea.ATTN_FP8_E4M3, qs=A, ks=A, vs=A, cu=A), ea.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=ea.ATTN_FP8_E4M3, qs=A, ks=A, vs=A, causal=1), ea.ATTN_ERR_UNSUPPORTED),
+])
+def test_fwd_validation(lib, kw, status):
+    assert fwd(lib, **kw) == status
+
+
+def prep(lib, q=A, k=A, v=A, q8=A, k8=A, v8=A, qs=A, ks=A, vs=A, B=1, Hq=2, Hkv=2, N=128, d=128):
+    P = ctypes.c_void_p
+    return lib.attn_fp8_prepare(P(q), P(k), P(v), P(q8), P(k8), P(v8), P(qs), P(ks), P(vs),
+                                B, Hq, Hkv, N, d, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), ea.ATTN_ERR_INVALID),
+    (dict(v8=0), ea.ATTN_ERR_INVALID),
+    (dict(ks=0), ea.ATTN_ERR_INVALID),
+    (dict(N=0), ea.ATTN_ERR_INVALID),
+    (dict(Hq=3, Hkv=2), ea.ATTN_ERR_INVALID),
+    (dict(d=64), ea.ATTN_ERR_UNSUPPORTED),
+    (dict(q8=A + 1), ea.ATTN_ERR_ALIGN),
+    (dict(k=A + 2), ea.ATTN_ERR_ALIGN),
+])
+def test_prepare_validation(lib, kw, status):
+    assert prep(lib, **kw) == status
