@@ -61,11 +61,14 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     case ATTN_BF16:
     case ATTN_FP16:
       if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
+      // the kernels address one head's K/V rows with 32-bit byte offsets
+      if ((long long)N * Hkv * d * 2 > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
       err = attn::launch_fwd_16bit(a, dtype == ATTN_BF16, stream);
       break;
     case ATTN_FP8_E4M3:
       if (!q_scale || !k_scale || !v_scale) return ATTN_ERR_INVALID;
       if (d != 128 || cu_seqlens != nullptr || causal) return ATTN_ERR_UNSUPPORTED;
+      if ((long long)N * Hkv * d > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
       err = attn::launch_fwd_fp8(a, stream);
       break;
     default:

@@ -87,34 +87,66 @@ __device__ __forceinline__ int xcd_remap(int wg, int total) {
   return x * q + (x < r ? x : r) + i;
 }
 
-// Position of key k (0..15 inside a 16-key group) in the permuted V^T tile: the order in
-// which the P^T accumulator registers are handed to the second MFMA (see file comment).
-__host__ __device__ constexpr int vpos16(int k) {
-  return 8 * ((k >> 2) & 1) + (k & 3) + 4 * (k >> 3);
+
+// ---- LDS tile layout -------------------------------------------------------------------------
+// A K or V tile of BC rows x D columns (16-bit) is stored as blocks of 16 rows; inside a block
+// the 16-byte chunks are chunk-major (chunk c of the 16 rows is contiguous) and the row order
+// inside a chunk column is XOR-ed with 4*(c mod 4).  With 64 LDS banks this makes both operand
+// reads conflict free: a b128 read of one chunk by 16 lanes (16 rows of K) and a b64
+// transpose read of 4 rows x 16 columns by 16 or 32 lanes (V).  The buffer-to-LDS copies write
+// 64 consecutive 16-byte positions per instruction, so the layout is produced by choosing, per
+// lane, which (row, chunk) of global memory it fetches.
+template <int D>
+__device__ __forceinline__ int tile_pos(int row, int chunk) {
+  constexpr int NCH = D / 8;
+  return (row >> 4) * 16 * NCH + chunk * 16 + ((row & 15) ^ (4 * (chunk & 3)));
+}
+template <int D>
+__device__ __forceinline__ void tile_row_chunk(int p, int& row, int& chunk) {
+  constexpr int NCH = D / 8;
+  const int blk = p / (16 * NCH), o = p % (16 * NCH);
+  chunk = o >> 4;
+  row = 16 * blk + ((o & 15) ^ (4 * (chunk & 3)));
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+// NI consecutive 1 KB buffer-to-LDS copies: copy i moves 16 bytes per lane from byte offset
+// voff[i] of the buffer [base, base + nbytes) to lds_dst + 1024*i + 16*lane.  Offsets at or
+// past nbytes read as zero.  (The buffer resource type exists only in the device pass, so
+// the host pass sees an empty body.)
+template <int NI>
+__device__ __forceinline__ void copy_rows_to_lds(const char* base, int nbytes, char* lds_dst, const int* voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, nbytes, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(void, lds_dst + 1024 * i), 16, voff[i], 0, 0, 0);
+#endif
 }
 
 template <int D, int BC, bool BF16, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void fwd_kernel(
+__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int N,
     const int* __restrict__ cu_seqlens, int nseq, float alpha, int num_qblocks) {
-  constexpr int KROW = D + 8;   // K tile row stride (elements); +16 B against bank conflicts
-  constexpr int VROW = BC + 8;  // V^T tile row stride (elements)
-  constexpr int STAGE = BC * KROW + D * VROW;
-  constexpr int KS_D = D / 16;   // k-steps of the first product (over d)
-  constexpr int KS_C = BC / 16;  // k-steps of the second product (over keys)
-  constexpr int NB_C = BC / 32;  // 32-key accumulator blocks per tile
-  constexpr int NB_D = D / 32;   // 32-wide d blocks of the O accumulator
-  constexpr int K_ITEMS = BC * D / 8;            // 16-byte chunks of a K tile
-  constexpr int K_PER = (K_ITEMS + kThreads - 1) / kThreads;
-  constexpr int V_ITEMS = (BC / 4) * (D / 8);    // (4 keys x 8 d) pieces of a V tile
-  constexpr int V_PER = (V_ITEMS + kThreads - 1) / kThreads;
-  static_assert(BC % 32 == 0 && D % 32 == 0, "tile shape");
+  constexpr int NCH = D / 8;                       // 16-byte chunks per row
+  constexpr int TILE_BYTES = BC * D * 2;
+  constexpr int NI = TILE_BYTES / 1024 / 4;        // 1 KB copy instructions per wave per tensor
+  constexpr int KS_D = D / 16;                     // k-steps of the first product (over d)
+  constexpr int KS_C = BC / 16;                    // k-steps of the second product (over keys)
+  constexpr int NB_C = BC / 32;                    // 32-key accumulator blocks per tile
+  constexpr int NB_D = D / 32;                     // 32-wide d blocks of the O accumulator
+  static_assert(BC % 32 == 0 && D % 32 == 0 && NI * 4 * 1024 == TILE_BYTES, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  // two stages, each K then V; separate objects so the compiler can tell the stages apart
+  __shared__ __attribute__((aligned(1024))) char st0[2 * TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char st1[2 * TILE_BYTES];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
 
   // ---- which (sequence, head, query block) ----
@@ -135,11 +167,12 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void fwd_kernel(
   const int q0 = qb * kBr;
   if (q0 >= n) return;  // whole workgroup: block lies past the end of this sequence
   const int g = h / (Hq / Hkv);
-  const int64_t qstride = (int64_t)Hq * D, kvstride = (int64_t)Hkv * D;
+  const int64_t qstride = (int64_t)Hq * D;
+  const int rowbytes = Hkv * D * 2;  // distance between consecutive tokens of one K/V head
 
-  // ---- Q fragment of this lane: query qi, d = 16*ks + 8*hi .. +7 ----
-  const int qw = q0 + wave * 32;     // first query of this wave
-  const int qi = qw + l32;           // this lane's query (within the sequence)
+  // ---- Q fragment of this lane: query qi, d = 16*st + 8*hi .. +7 ----
+  const int qw = q0 + wave * 32;
+  const int qi = qw + l32;
   u32x4 qf[KS_D];
   {
     const int row = qi < n ? qi : n - 1;
@@ -148,154 +181,136 @@ __global__ __launch_bounds__(kThreads, (D <= 128 ? 2 : 1)) void fwd_kernel(
     for (int s = 0; s < KS_D; ++s) qf[s] = *reinterpret_cast<const u32x4*>(qp + 16 * s);
   }
 
-  const uint16_t* kb = k + (int64_t)seq_start * kvstride + (int64_t)g * D;
-  const uint16_t* vb = v + (int64_t)seq_start * kvstride + (int64_t)g * D;
-  const int kv_end = CAUSAL ? min(n, q0 + kBr) : n;
-  const int ntiles = (kv_end + BC - 1) / BC;
-
-  u32x4 kreg[K_PER];
-  u32x4 vreg[V_PER][4];
-
-  auto load_tile = [&](int tile) {
-    const int k0 = tile * BC;
+  // ---- K/V copies: per-lane byte offsets inside a tile, one buffer resource per tile ----
+  int voff[NI];
 #pragma unroll
-    for (int i = 0; i < K_PER; ++i) {
-      const int c = tid + kThreads * i;
-      if (K_ITEMS % kThreads == 0 || c < K_ITEMS) {
-        const int row = c / (D / 8), col = c % (D / 8);
-        const int r = min(k0 + row, n - 1);
-        kreg[i] = *reinterpret_cast<const u32x4*>(kb + (int64_t)r * kvstride + col * 8);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < V_PER; ++i) {
-      const int c = tid + kThreads * i;
-      if (V_ITEMS % kThreads == 0 || c < V_ITEMS) {
-        const int run = c / (D / 8), dch = c % (D / 8);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int r = min(k0 + run * 4 + rr, n - 1);
-          vreg[i][rr] = *reinterpret_cast<const u32x4*>(vb + (int64_t)r * kvstride + dch * 8);
-        }
-      }
-    }
+  for (int i = 0; i < NI; ++i) {
+    int row, chunk;
+    tile_row_chunk<D>((wave * NI + i) * 64 + lane, row, chunk);
+    voff[i] = row * rowbytes + chunk * 16;
+  }
+  const char* kbase = reinterpret_cast<const char*>(k) + ((int64_t)seq_start * Hkv + g) * D * 2;
+  const char* vbase = reinterpret_cast<const char*>(v) + ((int64_t)seq_start * Hkv + g) * D * 2;
+  const int nbytes = (n - 1) * rowbytes + D * 2;  // bytes of this head's K (or V) rows
+  auto issue_tile = [&](char* stage, int tile) {
+    const int off = tile * BC * rowbytes;  // rows at or past n fall outside and read as zero
+    copy_rows_to_lds<NI>(kbase + off, nbytes - off, stage + wave * NI * 1024, voff);
+    copy_rows_to_lds<NI>(vbase + off, nbytes - off, stage + TILE_BYTES + wave * NI * 1024, voff);
   };
 
-  auto store_tile = [&](int buf) {
-    uint16_t* ks = smem + buf * STAGE;
-    uint16_t* vs = ks + BC * KROW;
+  // ---- operand read offsets (bytes inside a tile), lane part ----
+  // K (A operand of S^T = K Q^T): row 32*cb + l32, chunk 2*st + hi; the XOR term depends on st&1
+  int koff[2];
 #pragma unroll
-    for (int i = 0; i < K_PER; ++i) {
-      const int c = tid + kThreads * i;
-      if (K_ITEMS % kThreads == 0 || c < K_ITEMS) {
-        const int row = c / (D / 8), col = c % (D / 8);
-        *reinterpret_cast<u32x4*>(ks + row * KROW + col * 8) = kreg[i];
-      }
+  for (int e = 0; e < 2; ++e)
+    koff[e] = 16 * ((l32 >> 4) * 16 * NCH + (2 * e + hi) * 16 + ((lane & 15) ^ (4 * (2 * e + hi))));
+  // V (A operand of O^T = V^T P^T) by transpose reads: lane 16G + 4r + c reads 8 bytes of row
+  // 16*st + 4*(G/2) + 8*rd + r, chunk 4*db + 2*(G%2) + c/2, half c%2
+  int vtoff[2];
+  {
+    const int G = lane >> 4, r = (lane >> 2) & 3, c = lane & 3;
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      const int chunk = 2 * (G & 1) + (c >> 1);
+      const int rowm = 4 * (G >> 1) + 8 * rd + r;
+      vtoff[rd] = 16 * (chunk * 16 + (rowm ^ (4 * chunk))) + 8 * (c & 1);
     }
-#pragma unroll
-    for (int i = 0; i < V_PER; ++i) {
-      const int c = tid + kThreads * i;
-      if (V_ITEMS % kThreads == 0 || c < V_ITEMS) {
-        const int run = c / (D / 8), dch = c % (D / 8);
-        // keys 4*run .. 4*run+3 land on 4 consecutive permuted positions
-        const int pos = (run >> 2) * 16 + vpos16((run & 3) * 4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int w = e >> 1;
-          uint32_t p01, p23;
-          if (e & 1) {
-            p01 = (vreg[i][0][w] >> 16) | (vreg[i][1][w] & 0xFFFF0000u);
-            p23 = (vreg[i][2][w] >> 16) | (vreg[i][3][w] & 0xFFFF0000u);
-          } else {
-            p01 = (vreg[i][0][w] & 0xFFFFu) | (vreg[i][1][w] << 16);
-            p23 = (vreg[i][2][w] & 0xFFFFu) | (vreg[i][3][w] << 16);
-          }
-          u32x2 pr = {p01, p23};
-          *reinterpret_cast<u32x2*>(vs + (dch * 8 + e) * VROW + pos) = pr;
-        }
-      }
-    }
-  };
+  }
 
   f32x16 oacc[NB_D];
 #pragma unroll
   for (int i = 0; i < NB_D; ++i) oacc[i] = f32x16{};
-  float m = -INFINITY;  // running max of raw scores q.k
-  float l = 0.f;        // running sum over this lane's keys (the two halves are added at the end)
+  float m = -INFINITY;  // running max of raw scores q.k (the stabiliser; may trail the true max)
+  float l = 0.f;        // running sum over this lane's keys (lane halves are added at the end)
   const float c = alpha * kLog2e;
 
-  load_tile(0);
-  store_tile(0);
-  for (int j = 0; j < ntiles; ++j) {
-    if (j + 1 < ntiles) load_tile(j + 1);
-    __syncthreads();
-    const uint16_t* ks = smem + (j & 1) * STAGE;
-    const uint16_t* vs = ks + BC * KROW;
+  const int kv_end = CAUSAL ? min(n, q0 + kBr) : n;
+  const int ntiles = (kv_end + BC - 1) / BC;
+
+  auto compute_tile = [&](const char* stage, int j) {
+    const char* ks = stage;
+    const char* vs = stage + TILE_BYTES;
     const int k0 = j * BC;
-    const bool active = !CAUSAL || k0 <= qw + 31;
-    if (active) {
-      // S^T = K Q^T for this tile: lane holds query qi, keys k0 + 32*cb + 8*(r/4) + 4*hi + r%4
-      f32x16 s[NB_C];
+    // S^T = K Q^T: lane holds query qi, keys k0 + 32*cb + 8*(r/4) + 4*hi + r%4
+    f32x16 s[NB_C];
 #pragma unroll
-      for (int cb = 0; cb < NB_C; ++cb) {
-        s[cb] = f32x16{};
-        const uint16_t* arow = ks + (cb * 32 + l32) * KROW + 8 * hi;
+    for (int cb = 0; cb < NB_C; ++cb) {
+      s[cb] = f32x16{};
 #pragma unroll
-        for (int st = 0; st < KS_D; ++st)
-          s[cb] = mma32<BF16>(*reinterpret_cast<const u32x4*>(arow + 16 * st), qf[st], s[cb]);
+      for (int st = 0; st < KS_D; ++st) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(ks + koff[st & 1] + cb * 512 * NCH + 512 * (st & ~1));
+        s[cb] = mma32<BF16>(a, qf[st], s[cb]);
       }
-      const bool need_mask = (k0 + BC > n) || (CAUSAL && k0 + BC - 1 > qw);
-      if (need_mask) {
-#pragma unroll
-        for (int cb = 0; cb < NB_C; ++cb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + cb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-            if (key >= n || (CAUSAL && key > qi)) s[cb][r] = -INFINITY;
-          }
-      }
-      float mt = -INFINITY;
-#pragma unroll
-      for (int cb = 0; cb < NB_C; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[cb][r]);
-      mt = halves_max(mt);
-      const float mnew = fmaxf(m, mt);
-      const float mc = (mnew == -INFINITY) ? 0.f : mnew * c;
-      const float corr = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m * c - mc);
-      m = mnew;
-      float rs = 0.f;
+    }
+    const bool need_mask = (k0 + BC > n) || (CAUSAL && k0 + BC - 1 > qw);
+    if (need_mask) {
 #pragma unroll
       for (int cb = 0; cb < NB_C; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cb][r], c, -mc));
-          s[cb][r] = p;
-          rs += p;
+          const int key = k0 + cb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (key >= n || (CAUSAL && key > qi)) s[cb][r] = -INFINITY;
         }
-      l = l * corr + rs;
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int cb = 0; cb < NB_C; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[cb][r]);
+    mt = halves_max(mt);
+    // Rescale only when some row's maximum grew by more than 2^8 in the exp2 domain; otherwise
+    // keep the old stabiliser (P then stays below 2^8).  O / l and L are exact either way.
+    const float thr = (m == -INFINITY) ? -INFINITY : m * c + 8.f;
+    if (__builtin_amdgcn_ballot_w64(mt * c > thr)) {
+      const float mnew = fmaxf(m, mt);
+      const float corr = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - mnew) * c);
+      m = mnew;
+      l *= corr;
 #pragma unroll
       for (int db = 0; db < NB_D; ++db) oacc[db] *= corr;
-      // P^T as the B operand: k-step st takes accumulator registers 8*(st%2) .. +7 of block st/2
-      u32x4 pf[KS_C];
+    }
+    const float mc = (m == -INFINITY) ? 0.f : m * c;
+    float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
-      for (int st = 0; st < KS_C; ++st) {
-        const int cb = st >> 1, base = (st & 1) * 8;
-        pf[st] = u32x4{pack2<BF16>(s[cb][base + 0], s[cb][base + 1]),
-                       pack2<BF16>(s[cb][base + 2], s[cb][base + 3]),
-                       pack2<BF16>(s[cb][base + 4], s[cb][base + 5]),
-                       pack2<BF16>(s[cb][base + 6], s[cb][base + 7])};
+    for (int cb = 0; cb < NB_C; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cb][r], c, -mc));
+        s[cb][r] = p;
+        if (r & 1) rs1 += p; else rs0 += p;
       }
-      // O^T += V^T P^T
+    l += rs0 + rs1;
+    // O^T += V^T P^T; k-step st takes accumulator registers 8*(st%2) .. +7 of block st/2
+#pragma unroll
+    for (int st = 0; st < KS_C; ++st) {
+      const int cb = st >> 1, base = (st & 1) * 8;
+      const u32x4 pf = u32x4{pack2<BF16>(s[cb][base + 0], s[cb][base + 1]), pack2<BF16>(s[cb][base + 2], s[cb][base + 3]),
+                             pack2<BF16>(s[cb][base + 4], s[cb][base + 5]), pack2<BF16>(s[cb][base + 6], s[cb][base + 7])};
 #pragma unroll
       for (int db = 0; db < NB_D; ++db) {
-        const uint16_t* arow = vs + (db * 32 + l32) * VROW + 8 * hi;
-#pragma unroll
-        for (int st = 0; st < KS_C; ++st)
-          oacc[db] = mma32<BF16>(*reinterpret_cast<const u32x4*>(arow + 16 * st), pf[st], oacc[db]);
+        const int imm = st * 256 * NCH + db * 1024;
+        const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vs + vtoff[0] + imm));
+        const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vs + vtoff[1] + imm));
+        const u32x2 a0 = __builtin_bit_cast(u32x2, t0), a1 = __builtin_bit_cast(u32x2, t1);
+        oacc[db] = mma32<BF16>(u32x4{a0[0], a0[1], a1[0], a1[1]}, pf, oacc[db]);
       }
     }
-    if (j + 1 < ntiles) store_tile((j + 1) & 1);
+  };
+
+  // ---- main loop: two stages, unrolled by two so each half names its stage statically ----
+  issue_tile(st0, 0);
+  __builtin_amdgcn_s_waitcnt(0);  // Q fragments and tile 0 have arrived
+  __syncthreads();
+  for (int j = 0; j < ntiles; j += 2) {
+    if (j + 1 < ntiles) issue_tile(st1, j + 1);
+    if (!CAUSAL || j * BC <= qw + 31) compute_tile(st0, j);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (j + 1 >= ntiles) break;
+    if (j + 2 < ntiles) issue_tile(st0, j + 2);
+    if (!CAUSAL || (j + 1) * BC <= qw + 31) compute_tile(st1, j + 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   }
 
   // ---- epilogue: O / l, L = alpha*m + ln l ----

@@ -79,6 +79,9 @@ enum {
  * lse:     fp32, natural log, in units of the scaled scores S.  A row without visible keys
  *          gets O = 0 and L = -inf.
  *
+ * Limits: one head's K (or V) rows must span less than 2 GiB, i.e. N * Hkv * d * sizeof(element)
+ * < 2^31 (ATTN_ERR_UNSUPPORTED otherwise); B * N < 2^31 tokens.
+ *
  * Returns ATTN_OK or a negative status; on error nothing is enqueued.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -78,8 +78,31 @@ def gpu_rows(inp, o_gpu, lse_gpu, heads, tokens):
     return o, lse
 
 
+def half_ulp(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Half a unit in the last place of the output format at |x| (bf16: 8 significant bits,
+    fp16: 11), i.e. the largest error of rounding the exact result to that format."""
+    bits = {"bf16": 8, "fp16": 11}[dtype]
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    if dtype == "fp16":
+        e = np.maximum(e, -14.0)
+    return np.where(ax > 0, 2.0 ** (e - bits), 0.0)
+
+
+def metrics(o_test, o_ref, lse_test, lse_ref, dtype: str) -> dict:
+    """Error measures against the fp64 oracle.  ``max_abs_excess`` is the largest error left
+    after subtracting, element by element, the half ulp that rounding the exact O to the
+    output format costs on its own (for |O| >= 4 half a bf16 ulp is 0.0156, more than the
+    whole 1e-2 budget; this reading keeps 1e-2 as the bound on the kernel's own error)."""
+    m = oracle.error_metrics(o_test, o_ref, lse_test, lse_ref)
+    err = np.abs(np.asarray(o_test, dtype=np.float64) - np.asarray(o_ref, dtype=np.float64))
+    m["max_abs_excess"] = float(np.max(err - half_ulp(o_ref, dtype))) if err.size else 0.0
+    return m
+
+
 def check(metrics: dict, *, max_abs=TOL_MAX_ABS, rmse=TOL_RMSE, lse=TOL_LSE, what=""):
-    assert metrics["max_abs"] <= max_abs, f"{what}: O max-abs {metrics['max_abs']:.3e} > {max_abs}"
+    key = "max_abs_excess" if "max_abs_excess" in metrics else "max_abs"
+    assert metrics[key] <= max_abs, f"{what}: O {key} {metrics[key]:.3e} > {max_abs} ({metrics})"
     assert metrics["rmse"] <= rmse, f"{what}: O RMSE {metrics['rmse']:.3e} > {rmse}"
     if "lse_max_abs" in metrics and lse is not None:
         assert metrics["lse_max_abs"] <= lse, f"{what}: LSE error {metrics['lse_max_abs']:.3e} > {lse}"

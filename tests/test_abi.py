@@ -60,6 +60,7 @@ def fwd(lib, q=A, k=A, v=A, o=A, lse=A, B=1, Hq=2, Hkv=2, N=128, cu=None, d=128,
     (dict(alpha=float("inf")), ea.ATTN_ERR_INVALID),
     (dict(causal=2), ea.ATTN_ERR_INVALID),
     (dict(B=1 << 16, N=1 << 15), ea.ATTN_ERR_INVALID),
+    (dict(Hq=16, Hkv=16, N=1 << 20, d=128), ea.ATTN_ERR_UNSUPPORTED),  # one head's K spans >= 2 GiB
     (dict(q=A + 2), ea.ATTN_ERR_ALIGN),
     (dict(k=A + 8), ea.ATTN_ERR_ALIGN),
     (dict(v=A + 4), ea.ATTN_ERR_ALIGN),

@@ -8,8 +8,9 @@
   (first and last token of every sequence plus random ones), and every output is checked for
   a property that holds at any size (O inside the range of the V column, finite LSE).
 
-Tolerances (spec bars for bf16; fp16 uses the same): O max-abs <= 1e-2, RMSE <= 2e-3,
-LSE max-abs <= 1e-3.
+Tolerances (bf16 bars; fp16 uses the same): O max-abs <= 1e-2 beyond the half ulp that
+rounding the exact result to the output format costs by itself, O RMSE <= 2e-3, LSE max-abs
+<= 1e-3.
 """
 import numpy as np
 import pytest
@@ -27,7 +28,7 @@ def _compare_full(inp, what):
                  f"dtype={inp.dtype} seed={inp.seed} cu={None if inp.cu_seqlens is None else inp.cu_seqlens.tolist()}")
     o_gpu, lse_gpu = gu.run_gpu(inp)
     o_ref, lse_ref = gu.oracle_full(inp)
-    m = oracle.error_metrics(o_gpu, o_ref, lse_gpu, lse_ref)
+    m = gu.metrics(o_gpu, o_ref, lse_gpu, lse_ref, inp.dtype)
     gu.check(m, what=what)
     return m
 
@@ -86,7 +87,7 @@ def test_uniform_scores_give_mean(causal):
     cnt = np.arange(1, 334, dtype=np.float64) if causal else np.full(333, 333.0)
     mean = (np.cumsum(v, axis=1) / cnt[None, :, None, None]) if causal else \
         np.repeat(v.mean(axis=1, keepdims=True), 333, axis=1)
-    m = oracle.error_metrics(o, mean, lse, np.log(cnt)[None, None, :].repeat(2, 1))
+    m = gu.metrics(o, mean, lse, np.log(cnt)[None, None, :].repeat(2, 1), "bf16")
     gu.check(m, what=f"uniform causal={causal}")
 
 
@@ -108,4 +109,4 @@ def test_full_size_sampled(name):
     o_ref, lse_ref = oracle.attention_rows(q, k, v, heads, tokens, causal=inp.causal, alpha=inp.alpha,
                                            cu_seqlens=inp.cu_seqlens)
     o_s, lse_s = gu.gpu_rows(inp, o_gpu, lse_gpu, heads, tokens)
-    gu.check(oracle.error_metrics(o_s, o_ref, lse_s, lse_ref), what=name)
+    gu.check(gu.metrics(o_s, o_ref, lse_s, lse_ref, inp.dtype), what=name)
