@@ -29,18 +29,34 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 dense bf16 FLOP/clk/CU x 2.4 GHz
 WORKLOAD = dict(name="mha_n16384_b1_h16_d128", B=1, N=16384, H=16, d=128, causal=False, seed=2)
-# Traffic per launch measured by rocprofv3 --pmc (FETCH_SIZE / WRITE_SIZE) for the current kernel,
-# scaled by the copy-kernel calibration; None until taken for this kernel version.
-MEASURED_TRAFFIC_BYTES = None
+# HBM-side bytes per launch of the attention kernel from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE,
+# scaled by the counters of a copy kernel of known size (profiles/fwd_bf16_d128_n16384_traffic.md).
+# Valid only for the kernel source they were taken on; any other version reports null.
+MEASURED_TRAFFIC = {"kernel_source": "exact_attention_76_amd/csrc/attn_fwd.hip",
+                    "sha256_prefix": "21e9df9fc4856c3e", "bytes": 403843800}
+
+
+def measured_traffic():
+    import hashlib
+
+    path = os.path.join(ROOT, MEASURED_TRAFFIC["kernel_source"])
+    try:
+        digest = hashlib.sha256(open(path, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    return MEASURED_TRAFFIC["bytes"] if digest.startswith(MEASURED_TRAFFIC["sha256_prefix"]) else None
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="before timing, run one elementwise copy (negation) of this many MiB, so that "
+                         "profiler byte counters can be scaled against a kernel of known traffic")
     return ap.parse_args()
 
 
@@ -95,6 +111,13 @@ def main():
     def step():
         ea.attn_fwd(q, k, v, o, lse, causal=w["causal"], alpha=inp.alpha, stream=stream)
 
+    if args.calibration_copy_mib:
+        n_el = args.calibration_copy_mib * (1 << 20) // 2
+        src = torch.ones(n_el, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)  # reads and writes exactly calibration_copy_mib MiB each
+        torch.cuda.synchronize()
+        del src, dst
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
@@ -115,7 +138,7 @@ def main():
 
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": MEASURED_TRAFFIC_BYTES}
+                "traffic": measured_traffic()}
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, args.cpu_seconds)
