@@ -1,11 +1,438 @@
-// fp8.hip -- FP8 e4m3 forward pass and pre-pass (not yet built: both report "not supported").
+// fp8.hip -- the FP8 e4m3 path for gfx950: the pre-pass (incoherent processing + power-of-two
+// block quantisation) and the attention forward pass on e4m3 inputs.
+//
+// Sources: FlashAttention-3 pages, zenmind digest section 3.5 ("FP8 adaptation": block
+// quantisation with one scale per block of Q, K, V; incoherent processing with a random +-1
+// diagonal times a Hadamard matrix applied to Q and K; the in-kernel layout work for the second
+// product), and the blog article's FP8 section (power-of-two scales, uniform inside a block;
+// softmax and accumulation in fp32).
+//
+// gfx950 design (ours):
+//   * Pre-pass: one workgroup per (tensor, batch, head, 64-token block); four lanes per token
+//     row hold 32 elements each; the Walsh-Hadamard butterflies run in fp64 (five stages in
+//     registers, two across the lane quad), so the rotated values are exact; the block's
+//     largest magnitude picks the exponent and every element is rounded to e4m3 in software
+//     from its exact fp64 value.
+//   * Attention: the structure of the 16-bit kernel (128 queries per workgroup, scores formed
+//     transposed, online softmax in fp32, K/V tiles copied buffer-to-LDS, two LDS stages), with
+//     both products on v_mfma_scale_f32_32x32x64_f8f6f4.  The per-block power-of-two scales of
+//     Q, K and V go into the instruction's E8M0 scale operands, so they cost nothing.  P is
+//     quantised as e4m3 of 2^8 * P (the 2^8 rides in the exp2 argument and cancels against the
+//     row sum, which is summed from the unquantised values).  V is read transposed from LDS
+//     with ds_read_b64_tr_b8, the key order matching the byte order of the P operand.
 #include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
 
 #include "internal.h"
 
 namespace attn {
+namespace {
 
-hipError_t launch_fwd_fp8(const FwdArgs&, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_fp8_prepare(const PrepareArgs&, hipStream_t) { return hipErrorNotSupported; }
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ============================================================================================
+// Pre-pass
+// ============================================================================================
+
+struct PrepTensor {
+  const uint16_t* x;  // bf16 [B, N, H, 128]
+  uint8_t* x8;        // e4m3 codes, same layout
+  float* scale;       // [B, H, nblk]
+  int H;
+  int rotate;         // multiply by diag(signs) * Hadamard first
+  int scale_shift;    // log2 of the extra divisor folded into the scale (7 for rotated K)
+};
+
+// Nearest e4m3 (OCP, "fn") code to z, ties to the even code, sign kept, |z| clamped to 448.
+__device__ __forceinline__ uint32_t e4m3_rne(double z) {
+  const uint64_t bits = (uint64_t)__double_as_longlong(z);
+  const uint32_t sign = (uint32_t)(bits >> 56) & 0x80u;
+  const double a = fabs(z);
+  if (a >= 448.0) return sign | 0x7Eu;
+  if (a < 0.015625) {  // below 2^-6: the subnormal grid, step 2^-9 (code 8 is 2^-6 itself)
+    return sign | (uint32_t)rint(a * 512.0);
+  }
+  int E = (int)((__double_as_longlong(a) >> 52) & 0x7FF) - 1023;  // floor(log2 a), -6..8
+  // a * 2^(3 - E) lies in [8, 16): the 3-bit mantissa plus the implicit bit
+  double q = rint(a * __longlong_as_double((long long)(1023 + 3 - E) << 52));
+  if (q >= 16.0) {
+    q = 8.0;
+    E += 1;
+  }
+  return sign | (uint32_t)((E + 7) << 3) | ((uint32_t)q - 8u);
+}
+
+__device__ __forceinline__ double shfl_xor_d(double x, int mask) {
+  const long long v = __double_as_longlong(x);
+  const int lo = __shfl_xor((int)(v & 0xffffffff), mask);
+  const int hi = __shfl_xor((int)(v >> 32), mask);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+__global__ __launch_bounds__(256) void fp8_prepare_kernel(PrepTensor t0, PrepTensor t1, PrepTensor t2, int B, int N,
+                                                          int nblk, const signed char* __restrict__ signs) {
+  const PrepTensor t = blockIdx.y == 0 ? t0 : (blockIdx.y == 1 ? t1 : t2);
+  const int H = t.H;
+  if ((int)blockIdx.x >= B * H * nblk) return;  // this tensor has fewer heads than the grid
+  const int blk = blockIdx.x % nblk;
+  const int bh = blockIdx.x / nblk;
+  const int h = bh % H, b = bh / H;
+  const int tid = threadIdx.x;
+  const int r = tid >> 2, p = tid & 3;  // token row of the block, quarter of the 128 features
+  const int token = blk * 64 + r;
+  const bool valid = token < N;
+  const int64_t rowoff = ((int64_t)b * N + (valid ? token : 0)) * H + h;
+
+  double y[32];
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(t.x + rowoff * 128 + 32 * p);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 w = valid ? src[c] : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y[8 * c + 2 * e] = (double)__uint_as_float(w[e] << 16);
+        y[8 * c + 2 * e + 1] = (double)__uint_as_float(w[e] & 0xFFFF0000u);
+      }
+    }
+  }
+  if (t.rotate) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+      if (signs[32 * p + i] < 0) y[i] = -y[i];
+    // Walsh-Hadamard butterflies (a, b) -> (a + b, a - b) at strides 1 .. 64 over the 128
+    // features give y H with H[i][j] = (-1)^popcount(i & j); strides below 32 stay in a lane.
+#pragma unroll
+    for (int hs = 1; hs < 32; hs <<= 1)
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        if ((i & hs) == 0) {
+          const double a = y[i], c = y[i + hs];
+          y[i] = a + c;
+          y[i + hs] = a - c;
+        }
+#pragma unroll
+    for (int m = 1; m <= 2; m <<= 1) {  // strides 32 and 64: partner lane p ^ m
+      const bool upper = (p & m) != 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const double o = shfl_xor_d(y[i], m);
+        y[i] = upper ? o - y[i] : y[i] + o;
+      }
+    }
+  }
+  // block amax (exact, fp64)
+  double amax = 0.0;
+  if (valid) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(y[i]));
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) amax = fmax(amax, shfl_xor_d(amax, m));
+  __shared__ double wmax[4];
+  if ((tid & 63) == 0) wmax[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmax(fmax(wmax[0], wmax[1]), fmax(wmax[2], wmax[3]));
+  // smallest e with amax <= 448 * 2^e: amax = f * 2^ex, f in [0.5, 1); 448 = 0.875 * 2^9
+  int e = 0;
+  if (amax > 0.0) {
+    const long long bits = __double_as_longlong(amax);
+    const int ex = (int)((bits >> 52) & 0x7FF) - 1022;
+    const long long frac = bits & 0xFFFFFFFFFFFFFLL;  // f = (1 + frac / 2^52) / 2
+    e = (frac <= (3LL << 50)) ? ex - 9 : ex - 8;
+  }
+  const double inv = __longlong_as_double((long long)(1023 - e) << 52);  // 2^-e, exact
+  if (valid) {
+    uint32_t w[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      w[j] = e4m3_rne(y[4 * j] * inv) | (e4m3_rne(y[4 * j + 1] * inv) << 8) | (e4m3_rne(y[4 * j + 2] * inv) << 16) |
+             (e4m3_rne(y[4 * j + 3] * inv) << 24);
+    u32x4* dst = reinterpret_cast<u32x4*>(t.x8 + rowoff * 128 + 32 * p);
+    dst[0] = u32x4{w[0], w[1], w[2], w[3]};
+    dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+  }
+  if (tid == 0) t.scale[((int64_t)b * H + h) * nblk + blk] = __uint_as_float((uint32_t)(e - t.scale_shift + 127) << 23);
+}
+
+// ============================================================================================
+// Attention on e4m3 inputs
+// ============================================================================================
+
+constexpr int kThreads = 256;
+constexpr int kBr = 128;  // queries per workgroup, 32 per wave
+constexpr int kD = 128;   // head dim (bytes per row of an e4m3 tile)
+constexpr int kBc = 64;   // keys per tile = one scale block
+constexpr int kTile = kBc * kD;      // bytes of one K or V tile
+constexpr int kNI = kTile / 1024 / 4;  // 1 KB copies per wave per tensor
+
+// LDS tile layout: blocks of 16 rows, chunk-major inside a block (16-byte chunks), rows inside
+// a chunk column XOR-ed with 4*(chunk & 1).  Conflict free for 16-lane b128 reads of one chunk
+// (K) and for 32-lane ds_read_b64_tr_b8 reads of 8 rows x 32 bytes (V).
+__device__ __forceinline__ void f8_tile_row_chunk(int p, int& row, int& chunk) {
+  const int blk = p >> 7, o = p & 127;
+  chunk = o >> 4;
+  row = 16 * blk + ((o & 15) ^ (4 * (chunk & 1)));
+}
+
+template <int NI>
+__device__ __forceinline__ void copy_rows_to_lds8(const char* base, int nbytes, char* lds_dst, const int* voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, nbytes, 0x00020000);
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(void, lds_dst + 1024 * i), 16, voff[i], 0, 0, 0);
+#endif
+}
+
+__device__ __forceinline__ f32x16 mma_f8(i32x8 a, i32x8 b, f32x16 c, int sa, int sb) {
+  // format 0 = e4m3 for both operands; sa / sb are E8M0 power-of-two scales
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+__device__ __forceinline__ int e8m0_of(float pow2) { return (int)((__float_as_uint(pow2) >> 23) & 0xFF); }
+
+__device__ __forceinline__ float halves_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ int xcd_remap(int wg, int total) {
+  constexpr int kXcd = 8;
+  const int q = total / kXcd, r = total % kXcd;
+  const int x = wg % kXcd, i = wg / kXcd;
+  return x * q + (x < r ? x : r) + i;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
+    const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
+    const float* __restrict__ qs, const float* __restrict__ ks_, const float* __restrict__ vs_,
+    uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int N, float alpha, int num_qblocks) {
+  __shared__ __attribute__((aligned(1024))) char st0[2 * kTile];
+  __shared__ __attribute__((aligned(1024))) char st1[2 * kTile];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int nblk = (N + 63) / 64;
+
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int qb = logical % num_qblocks;
+  const int bh = logical / num_qblocks;
+  const int h = bh % Hq, b = bh / Hq;
+  const int n = N, seq_start = b * N;
+  const int q0 = qb * kBr;
+  const int g = h / (Hq / Hkv);
+  const int qw = q0 + wave * 32;
+  const int qi = qw + l32;
+  if (q0 >= n) return;
+
+  // Q fragment: query qi, bytes 64*st + 32*hi .. +31
+  i32x8 qf[2];
+  {
+    const int row = qi < n ? qi : n - 1;
+    const u32x4* qp = reinterpret_cast<const u32x4*>(q + ((int64_t)(seq_start + row) * Hq + h) * kD + 32 * hi);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const u32x4 a = qp[4 * s], c = qp[4 * s + 1];
+      qf[s] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)c[0], (int)c[1], (int)c[2], (int)c[3]};
+    }
+  }
+  const int qblock = (qw < n ? qw : n - 1) / 64;
+  const int sq = e8m0_of(qs[((int64_t)b * Hq + h) * nblk + qblock]);
+  const float* ksc = ks_ + ((int64_t)b * Hkv + g) * nblk;
+  const float* vsc = vs_ + ((int64_t)b * Hkv + g) * nblk;
+
+  const int rowbytes = Hkv * kD;
+  int voff[kNI];
+#pragma unroll
+  for (int i = 0; i < kNI; ++i) {
+    int row, chunk;
+    f8_tile_row_chunk((wave * kNI + i) * 64 + lane, row, chunk);
+    voff[i] = row * rowbytes + chunk * 16;
+  }
+  const char* kbase = reinterpret_cast<const char*>(k) + ((int64_t)seq_start * Hkv + g) * kD;
+  const char* vbase = reinterpret_cast<const char*>(v) + ((int64_t)seq_start * Hkv + g) * kD;
+  const int nbytes = (n - 1) * rowbytes + kD;
+  auto issue_tile = [&](char* stage, int tile) {
+    const int off = tile * kBc * rowbytes;
+    copy_rows_to_lds8<kNI>(kbase + off, nbytes - off, stage + wave * kNI * 1024, voff);
+    copy_rows_to_lds8<kNI>(vbase + off, nbytes - off, stage + kTile + wave * kNI * 1024, voff);
+  };
+
+  // K operand: row 32*cb + l32, chunks 4*st + 2*hi + e (e = 0, 1)
+  int koff[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) koff[e] = 16 * ((l32 >> 4) * 128 + (2 * hi + e) * 16 + ((lane & 15) ^ (4 * e)));
+  // V operand by transpose reads: lane 16G + 2r + c reads 8 bytes (half c) of row
+  // 16u + 4*(G/2) + 8*(r/4) + r%4, chunk 2*db + (G%2)
+  int vtoff;
+  {
+    const int G = lane >> 4, r = (lane >> 1) & 7, c = lane & 1;
+    const int rowm = 4 * (G >> 1) + 8 * (r >> 2) + (r & 3);
+    vtoff = 16 * ((G & 1) * 16 + (rowm ^ (4 * (G & 1)))) + 8 * c;
+  }
+
+  f32x16 oacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) oacc[i] = f32x16{};
+  float m = -INFINITY;
+  float l = 0.f;
+  const float c = alpha * kLog2e;
+  const int ntiles = (n + kBc - 1) / kBc;
+
+  auto compute_tile = [&](const char* stage, int j) {
+    const char* kt = stage;
+    const char* vt = stage + kTile;
+    const int k0 = j * kBc;
+    const int sk = e8m0_of(ksc[j]);
+    const int sv = e8m0_of(vsc[j]);
+    f32x16 s[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      s[cb] = f32x16{};
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(kt + koff[0] + cb * 4096 + st * 1024);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(kt + koff[1] + cb * 4096 + st * 1024);
+        const i32x8 a = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+        s[cb] = mma_f8(a, qf[st], s[cb], sk, sq);
+      }
+    }
+    if (k0 + kBc > n) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (k0 + cb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3) >= n) s[cb][r] = -INFINITY;
+    }
+    float mt = -INFINITY;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[cb][r]);
+    mt = halves_max(mt);
+    // P' = 2^8 * exp2((s - m) c) must stay below 448 (largest e4m3): rescale once some row's
+    // maximum exceeds the stabiliser by more than 0.75 in the exp2 domain.
+    const float thr = (m == -INFINITY) ? -INFINITY : m * c + 0.75f;
+    if (__builtin_amdgcn_ballot_w64(mt * c > thr)) {
+      const float mnew = fmaxf(m, mt);
+      const float corr = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - mnew) * c);
+      m = mnew;
+      l *= corr;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[db] *= corr;
+    }
+    const float mc = ((m == -INFINITY) ? 0.f : m * c) - 8.f;
+    float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cb][r], c, -mc));
+        s[cb][r] = p;
+        if (r & 1) rs1 += p; else rs0 += p;
+      }
+    l += rs0 + rs1;
+    // P'^T as the B operand: byte 16*cb + r holds accumulator register r of block cb
+    i32x8 pf;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int cb = w >> 2, r0 = 4 * (w & 3);
+      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[cb][r0], s[cb][r0 + 1], 0, false);
+      pf[w] = __builtin_amdgcn_cvt_pk_fp8_f32(s[cb][r0 + 2], s[cb][r0 + 3], lo, true);
+    }
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      i32x8 a;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const i32x2 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i32x2, vt + vtoff + u * 2048 + db * 512));
+        a[2 * u] = t[0];
+        a[2 * u + 1] = t[1];
+      }
+      oacc[db] = mma_f8(a, pf, oacc[db], sv, 127);
+    }
+  };
+
+  issue_tile(st0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int j = 0; j < ntiles; j += 2) {
+    if (j + 1 < ntiles) issue_tile(st1, j + 1);
+    compute_tile(st0, j);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (j + 1 >= ntiles) break;
+    if (j + 2 < ntiles) issue_tile(st0, j + 2);
+    compute_tile(st1, j + 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  const float lt = halves_sum(l);
+  if (qi < n) {
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    uint16_t* op = o + ((int64_t)(seq_start + qi) * Hq + h) * kD + 4 * hi;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        u32x2 pr = {pack_bf16x2(oacc[db][4 * gq + 0] * inv, oacc[db][4 * gq + 1] * inv),
+                    pack_bf16x2(oacc[db][4 * gq + 2] * inv, oacc[db][4 * gq + 3] * inv)};
+        *reinterpret_cast<u32x2*>(op + db * 32 + gq * 8) = pr;
+      }
+    if (hi == 0) {
+      // l carries the factor 2^8 of P'
+      lse[((int64_t)b * Hq + h) * N + qi] = lt > 0.f ? m * alpha + __logf(lt) - 8.f * kLn2 : -INFINITY;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fp8_prepare(const PrepareArgs& a, hipStream_t stream) {
+  const int nblk = (a.N + 63) / 64;
+  const bool rot = a.signs != nullptr;
+  PrepTensor tq{static_cast<const uint16_t*>(a.q), static_cast<uint8_t*>(a.q8), a.q_scale, a.Hq, rot, 0};
+  PrepTensor tk{static_cast<const uint16_t*>(a.k), static_cast<uint8_t*>(a.k8), a.k_scale, a.Hkv, rot, rot ? 7 : 0};
+  PrepTensor tv{static_cast<const uint16_t*>(a.v), static_cast<uint8_t*>(a.v8), a.v_scale, a.Hkv, 0, 0};
+  const long long grid = (long long)a.B * a.Hq * nblk;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(fp8_prepare_kernel, dim3((unsigned)grid, 3), dim3(256), 0, stream, tq, tk, tv, a.B, a.N, nblk,
+                     a.signs);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream) {
+  const int nqb = (a.N + kBr - 1) / kBr;
+  const long long grid = (long long)nqb * a.Hq * a.B;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(fwd_fp8_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream,
+                     static_cast<const uint8_t*>(a.q), static_cast<const uint8_t*>(a.k),
+                     static_cast<const uint8_t*>(a.v), a.q_scale, a.k_scale, a.v_scale,
+                     static_cast<uint16_t*>(a.o), a.lse, a.Hq, a.Hkv, a.N, a.alpha, nqb);
+  return hipGetLastError();
+}
 
 }  // namespace attn

@@ -148,20 +148,25 @@ def outlier_channels(rng: np.random.Generator, H: int, d: int, fraction: float =
 
 
 def fp8_inputs(B: int, N: int, H: int, d: int, *, seed: int = 5, outlier_scale: float = 20.0,
-               fraction: float = 0.001) -> AttnInputs:
-    """bf16 Q, K, V i.i.d. N(0,1) with a few feature channels (same ones in Q, K and V) scaled
-    by ``outlier_scale`` before the bf16 rounding.  Channel indices are drawn after Q, K, V."""
+               fraction: float = 0.001, independent_channels: bool = False) -> AttnInputs:
+    """bf16 Q, K, V i.i.d. N(0,1) with a fraction of the H*d feature channels scaled by
+    ``outlier_scale`` before the bf16 rounding.  Channel indices are drawn after Q, K, V: one
+    set shared by Q, K and V, or (``independent_channels``) one draw per tensor in the order
+    Q, K, V."""
     rng = np.random.default_rng(seed)
     q = rng.standard_normal((B, N, H, d), dtype=np.float32)
     k = rng.standard_normal((B, N, H, d), dtype=np.float32)
     v = rng.standard_normal((B, N, H, d), dtype=np.float32)
-    ch = outlier_channels(rng, H, d, fraction)
+    shared = outlier_channels(rng, H, d, fraction)
+    chans = []
     for t in (q, k, v):
+        ch = outlier_channels(rng, H, d, fraction) if independent_channels and chans else shared
+        chans.append(ch)
         flat = t.reshape(B, N, H * d)
         flat[:, :, ch] *= np.float32(outlier_scale)
     inp = AttnInputs(f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v), "bf16",
                      B, N, H, H, d, False, None, seed)
-    inp.meta["outlier_channels"] = ch
+    inp.meta["outlier_channels"] = chans[0] if not independent_channels else chans
     return inp
 
 

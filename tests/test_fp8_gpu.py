@@ -1,0 +1,157 @@
+"""GPU parity of the FP8 path.
+
+* attn_fp8_prepare against the oracle's emulation (oracle/fp8.py): e4m3 codes and block scales
+  must match bit for bit (integer work decided from exact fp64 values on both sides), with and
+  without the Hadamard rotation, for ragged token counts, grouped heads and the full workload.
+* attn_fwd on e4m3 inputs against the fp64 oracle run on the *unquantised* bf16 inputs (the
+  error measure of the FlashAttention-3 digest's section 3.5 / Table 3): O RMSE <= 3e-2, or the
+  floor that quantising the inputs sets for any implementation (exact attention on the
+  dequantised inputs) plus 2e-3 where that floor is higher.  The kernel's own error (against
+  the oracle run on its dequantised inputs) is bounded separately.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+from oracle import fp8 as ofp8
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev_bf16(bits):
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def gpu_prepare(inp, signs):
+    import exact_attention_76_amd as ea
+
+    q, k, v = (_dev_bf16(getattr(inp, n)) for n in "qkv")
+    sg = None if signs is None else torch.from_numpy(signs).cuda()
+    out = ea.fp8_prepare(q, k, v, hadamard_signs=sg)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_prepare(inp, signs):
+    q, k, v = (oracle.bf16_to_f64(getattr(inp, n)) for n in "qkv")
+    return ofp8.fp8_prepare(q, k, v, signs)
+
+
+def _assert_prepare_equal(got, want, what):
+    names = ["q8", "k8", "v8", "q_scale", "k_scale", "v_scale"]
+    for name, g, w in zip(names, got, want):
+        g = g.cpu().numpy()
+        if name.endswith("8"):
+            bad = np.argwhere(g != w)
+            assert bad.size == 0, f"{what}: {name} differs at {len(bad)} places, first {bad[:3].tolist()}"
+        else:
+            assert np.array_equal(g, w.astype(np.float32)), f"{what}: {name} differs"
+
+
+@pytest.mark.parametrize("rotate", [True, False])
+def test_prepare_bit_exact_ragged_gqa(rotate):
+    inp = si.dense_inputs(2, 100, 4, 128, Hkv=2, seed=600)
+    # widen the value range so several block exponents occur
+    inp.q = si.f32_to_bf16_bits(si.bf16_bits_to_f32(inp.q) * np.float32(37.0))
+    signs = si.hadamard_signs(128, seed=55) if rotate else None
+    gu.say("fp8 prepare ragged/GQA", rotate)
+    _assert_prepare_equal(gpu_prepare(inp, signs), oracle_prepare(inp, signs), f"prepare rotate={rotate}")
+
+
+def test_prepare_bit_exact_full_workload():
+    inp = si.CONFIGS["fp8_b2_h16_n8192_d128"]()
+    signs = si.hadamard_signs(128, seed=55)
+    gu.say("fp8 prepare full workload")
+    _assert_prepare_equal(gpu_prepare(inp, signs), oracle_prepare(inp, signs), "prepare full")
+
+
+def gpu_fp8_attention(inp, signs):
+    import exact_attention_76_amd as ea
+
+    q8, k8, v8, qs, ks, vs = gpu_prepare(inp, signs)
+    o, lse = ea.attention(q8, k8, v8, causal=False, alpha=inp.alpha, q_scale=qs, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    return o.double().cpu().numpy(), lse.double().cpu().numpy(), (q8, k8, v8, qs, ks, vs)
+
+
+def _three_errors(inp, o, lse, prep, heads, tokens):
+    """On the same rows: kernel vs fp64 on the unquantised inputs (X), exact attention on the
+    dequantised inputs vs the same (Y, the floor the input quantisation sets for any
+    implementation), and kernel vs exact attention on its own dequantised inputs (Z, the
+    kernel's own error: P rounded to e4m3 and fp32 arithmetic)."""
+    q8, k8, v8, qs, ks, vs = (t.cpu().numpy() for t in prep)
+    qd, kd, vd = ofp8.dequantize(q8, qs), ofp8.dequantize(k8, ks), ofp8.dequantize(v8, vs)
+    q, k, v = gu.widened(inp)
+    o_ref, lse_ref = oracle.attention_rows(q, k, v, heads, tokens, causal=False, alpha=inp.alpha)
+    o_dq, lse_dq = oracle.attention_rows(qd, kd, vd, heads, tokens, causal=False, alpha=inp.alpha)
+    o_s, lse_s = gu.gpu_rows(inp, o, lse, heads, tokens)
+    X = oracle.error_metrics(o_s, o_ref, lse_s, lse_ref)
+    Y = oracle.error_metrics(o_dq, o_ref, lse_dq, lse_ref)
+    Z = oracle.error_metrics(o_s, o_dq, lse_s, lse_dq)
+    gu.say("fp8 kernel vs fp64", X)
+    gu.say("fp8 quantised-input floor vs fp64", Y)
+    gu.say("fp8 kernel vs dequantised-input oracle", Z)
+    return X, Y, Z, lse_dq
+
+
+# Kernel's own error budget (Z): P is rounded to e4m3 (relative step 2^-3, so at most 2^-4 per
+# weight) before the second product; averaged over a row this stays well under the bar.
+TOL_FP8_OWN_RMSE = 1e-2
+
+
+def own_lse_bound(lse_dq):
+    """LSE budget of the kernel against the dequantised-input oracle.  The scores are exact
+    products of e4m3 values, but the matrix core sums the 64 products of one fp8 instruction
+    with less than fp32 precision (without the rotation, where one outlier product dominates a
+    dot product, errors of about 2^-12 of the score were measured); a softmax moves its LSE by
+    at most the largest score error.  So: 1e-3, or 2^-12 of the largest |L|, whichever is more."""
+    return max(gu.TOL_LSE, 2.0 ** -12 * float(np.max(np.abs(lse_dq))))
+
+
+def check_fp8(X, Y, Z, lse_dq):
+    """X: kernel vs fp64; Y: input-quantisation floor vs fp64; Z: kernel vs dequantised oracle.
+    The bar is RMSE <= 3e-2 against fp64 on the unquantised inputs; where quantising the inputs
+    alone (Y) already costs more than that, no implementation can meet it, and the kernel is
+    held to Y plus 2e-3 instead."""
+    assert Z["rmse"] <= TOL_FP8_OWN_RMSE, Z
+    assert Z["lse_max_abs"] <= own_lse_bound(lse_dq), (Z, own_lse_bound(lse_dq))
+    assert X["rmse"] <= max(gu.TOL_FP8_RMSE, Y["rmse"] + 2e-3), (X, Y)
+
+
+@pytest.mark.parametrize("rotate", [True, False])
+def test_fp8_attention_small(rotate):
+    inp = si.fp8_inputs(2, 300, 4, 128, seed=601, fraction=0.002)
+    signs = si.hadamard_signs(128, seed=55) if rotate else None
+    gu.say("fp8 attention small", rotate)
+    o, lse, prep = gpu_fp8_attention(inp, signs)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    T = inp.B * inp.N
+    heads, tokens = np.repeat(np.arange(inp.Hq), T), np.tile(np.arange(T), inp.Hq)  # every row
+    check_fp8(*_three_errors(inp, o, lse, prep, heads, tokens))
+
+
+def _full(inp, rows):
+    signs = si.hadamard_signs(128, seed=55)
+    o, lse, prep = gpu_fp8_attention(inp, signs)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    heads, tokens = gu.sample_rows(inp, rows, seed=2)
+    return _three_errors(inp, o, lse, prep, heads, tokens)
+
+
+def test_fp8_attention_full_workload():
+    """B=2, H=16, N=8192, d=128 with two x20 outlier channels shared by Q, K and V."""
+    inp = si.CONFIGS["fp8_b2_h16_n8192_d128"]()
+    gu.say("fp8 attention full workload")
+    check_fp8(*_full(inp, 2048))
+
+
+def test_fp8_attention_full_workload_independent_outliers():
+    """The other reading of the outlier construction: independent channel draws for Q, K, V."""
+    inp = si.fp8_inputs(2, 8192, 16, 128, seed=5, independent_channels=True)
+    gu.say("fp8 attention full workload, independent outlier channels")
+    X, Y, Z, lse_dq = _full(inp, 2048)
+    check_fp8(X, Y, Z, lse_dq)
+    assert X["rmse"] <= gu.TOL_FP8_RMSE, X
