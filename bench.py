@@ -1,18 +1,26 @@
 #!/usr/bin/env python3
 """Benchmark of the fused attention forward pass on one MI355X.
 
-One step = one attn_fwd call over the whole workload (inputs already resident in HBM).
-Workload: non-causal multi-head attention, bf16, B=1, N=16384, H=16, d=128 -- the longest
-point of the B*N = 16384-token sweep (the pages quote their d=128 non-causal figure at 16k).
+One step = one attn_fwd call over the whole workload, inputs already resident in HBM.
+Default workload (the headline line): non-causal multi-head attention, bf16, B=1, N=16384,
+H=16, d=128 -- the longest point of the B*N = 16384-token sweep (the pages quote their d=128
+non-causal figure at 16k).  ``--workload`` selects the other measured configurations:
+
+  sweep   bf16 non-causal d=128 H=16, N in 512..16384 with B*N = 16384 (one line per N)
+  causal  bf16 causal B=2 H=16 N=8192, d in 64/128/256 (one line per d)
+  varlen  bf16 causal GQA (Hq=32, Hkv=8, d=128), 8 packed sequences of 256..8192 tokens
+  fp8     e4m3 non-causal B=2 H=16 N=8192 d=128 on pre-quantised inputs; the FP8 pre-pass
+          (Hadamard rotation + block quantisation, HBM-bound) is timed separately
 
 Metric (FlashAttention-3 digest, section 7.1): TFLOPs/s with FLOPs = 4 * B * H * N^2 * d
-(halved when causal), and the fraction of MI355X dense bf16 MFMA peak.
+(halved when causal; summed per sequence for packed inputs), and the fraction of MI355X dense
+MFMA peak (bf16 2516.6, fp8 5033.2 TFLOP/s at 2.4 GHz, 256 CUs).
 
-Prints ONE JSON line with, besides the contract fields,
-  roofline     -- the attention kernel's algorithmic FLOPs per launch over its mean launch
-                  time (HIP events on the stream the kernel runs on) against the bf16 peak;
-  cpu_baseline -- the fp64 CPU oracle timed on a bounded sample of query rows of the same
-                  workload, as attention-FLOP throughput.
+Each line carries
+  roofline     -- algorithmic FLOPs per launch over the kernel's mean launch time, measured
+                  with HIP events on the stream the kernel runs on, against the dtype's peak;
+  cpu_baseline -- (headline only) the fp64 CPU oracle timed on a bounded sample of query rows
+                  of the same workload, as attention-FLOP throughput.
 """
 from __future__ import annotations
 
@@ -27,8 +35,9 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4096 dense bf16 FLOP/clk/CU x 2.4 GHz
-WORKLOAD = dict(name="mha_n16384_b1_h16_d128", B=1, N=16384, H=16, d=128, causal=False, seed=2)
+METRIC = "attention fwd TFLOPs/s (4·B·H·N²·d, ½ if causal) and % of MI355X MFMA peak"
+PEAK = {"bf16": 2516.6, "fp8": 5033.2}  # dense MFMA TFLOP/s: 256 CU x (4096 | 8192) FLOP/clk x 2.4 GHz
+HBM_PEAK_GBS = 8000.0
 # HBM-side bytes per launch of the attention kernel from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE,
 # scaled by the counters of a copy kernel of known size (profiles/fwd_bf16_d128_n16384_traffic.md).
 # Valid only for the kernel source they were taken on; any other version reports null.
@@ -52,6 +61,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="mha16k", choices=["mha16k", "sweep", "causal", "varlen", "fp8"])
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -81,10 +91,111 @@ def cpu_baseline(inp, target_s: float) -> dict:
         el = time.perf_counter() - t0
         if el >= target_s or el >= 30.0:
             break
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+    return {"value": float(f"{flops / el / 1e12:.4g}"), "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{rows} random (head, query) rows of the same workload, all keys each, fp64, "
-                      f"{el:.1f} s"}
+            "sample": f"{rows} random (head, query) rows of the same workload, all keys each, fp64, {el:.1f} s"}
+
+
+def timed(step, stream, steps, warmup):
+    """W untimed steps, then K steps between two synchronisations.  Returns (wall ms per step,
+    event ms per step measured on ``stream``)."""
+    import torch
+
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return wall, ev0.elapsed_time(ev1) / steps
+
+
+def to_dev(bits, dtype, dev):
+    import torch
+
+    t = torch.from_numpy(bits.view(np.int16))
+    return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16).to(dev)
+
+
+def line(args, name, inp, flops, ms_wall, ms_gpu, dtype, extra=None, traffic=None, cpu=None):
+    peak = PEAK[dtype]
+    tflops = flops / (ms_wall * 1e-3) / 1e12
+    achieved = flops / (ms_gpu * 1e-3) / 1e12
+    cfg = {"workload": name, "B": inp.B, "N": inp.N, "Hq": inp.Hq, "Hkv": inp.Hkv, "d": inp.d,
+           "causal": inp.causal, "varlen": inp.cu_seqlens is not None, "tokens": inp.total_tokens,
+           "flops_per_step": flops, "pct_of_peak": round(100 * tflops / peak, 2), "parallelism": "single GPU"}
+    if extra:
+        cfg.update(extra)
+    return {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_wall, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dtype, "data": "synthetic", "config": cfg,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+
+
+def run_16bit(args, name, inp, dev, stream, traffic=None, cpu=False):
+    import torch
+
+    import exact_attention_76_amd as ea
+
+    q, k, v = (to_dev(getattr(inp, n), inp.dtype, dev) for n in "qkv")
+    o = torch.empty_like(q)
+    if inp.cu_seqlens is None:
+        lse = torch.empty((inp.B, inp.Hq, inp.N), dtype=torch.float32, device=dev)
+        cu = None
+    else:
+        lse = torch.empty((inp.Hq, inp.total_tokens), dtype=torch.float32, device=dev)
+        cu = torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(dev)
+
+    def step():
+        ea.attn_fwd(q, k, v, o, lse, causal=inp.causal, alpha=inp.alpha, cu_seqlens=cu,
+                    max_seqlen=inp.N if cu is not None else None, stream=stream)
+
+    ms_wall, ms_gpu = timed(step, stream, args.steps, args.warmup)
+    cpu_res = cpu_baseline(inp, args.cpu_seconds) if cpu and not args.no_cpu_baseline else None
+    return line(args, name, inp, inp.flops(), ms_wall, ms_gpu, inp.dtype, traffic=traffic, cpu=cpu_res)
+
+
+def run_fp8(args, dev, stream):
+    import torch
+
+    import exact_attention_76_amd as ea
+    import seeded_inputs as si
+
+    inp = si.CONFIGS["fp8_b2_h16_n8192_d128"]()
+    q, k, v = (to_dev(getattr(inp, n), "bf16", dev) for n in "qkv")
+    signs = torch.from_numpy(si.hadamard_signs(inp.d)).to(dev)
+    q8, k8, v8, qs, ks, vs = ea.fp8_prepare(q, k, v, hadamard_signs=signs, stream=stream)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((inp.B, inp.Hq, inp.N), dtype=torch.float32, device=dev)
+
+    def attn():
+        ea.attn_fwd(q8, k8, v8, o, lse, alpha=inp.alpha, q_scale=qs, k_scale=ks, v_scale=vs, stream=stream)
+
+    def prep():
+        ea.attn_fp8_prepare(q, k, v, q8, k8, v8, qs, ks, vs, hadamard_signs=signs, stream=stream)
+
+    ms_wall, ms_gpu = timed(attn, stream, args.steps, args.warmup)
+    pw, pg = timed(prep, stream, args.steps, args.warmup)
+    nblk = -(-inp.N // 64)
+    prep_bytes = 3 * q.numel() * 2 + 3 * q.numel() + 3 * inp.B * inp.Hq * nblk * 4 + inp.d
+    extra = {"attention_only": True, "hadamard": True,
+             "prepare_ms": round(pw, 4),
+             "prepare_roofline": {"bound": "hbm", "achieved": round(prep_bytes / (pg * 1e-3) / 1e9, 1),
+                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": round(prep_bytes / (pg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                  "traffic": None, "bytes_per_launch": prep_bytes},
+             "prepare_plus_attention_tflops": round(inp.flops() / ((pw + ms_wall) * 1e-3) / 1e12, 2)}
+    return line(args, "fp8_b2_h16_n8192_d128", inp, inp.flops(), ms_wall, ms_gpu, "fp8", extra=extra)
 
 
 def main():
@@ -96,21 +207,10 @@ def main():
 
     import torch
 
-    import exact_attention_76_amd as ea
     import seeded_inputs as si
 
-    w = WORKLOAD
-    inp = si.dense_inputs(w["B"], w["N"], w["H"], w["d"], causal=w["causal"], seed=w["seed"])
     dev = torch.device("cuda:0")
-    q, k, v = (torch.from_numpy(getattr(inp, n).view(np.int16)).view(torch.bfloat16).to(dev) for n in "qkv")
-    o = torch.empty_like(q)
-    lse = torch.empty((w["B"], w["H"], w["N"]), dtype=torch.float32, device=dev)
     stream = torch.cuda.Stream(device=dev)  # default priority
-    flops = inp.flops()
-
-    def step():
-        ea.attn_fwd(q, k, v, o, lse, causal=w["causal"], alpha=inp.alpha, stream=stream)
-
     if args.calibration_copy_mib:
         n_el = args.calibration_copy_mib * (1 << 20) // 2
         src = torch.ones(n_el, dtype=torch.bfloat16, device=dev)
@@ -118,44 +218,23 @@ def main():
         torch.neg(src, out=dst)  # reads and writes exactly calibration_copy_mib MiB each
         torch.cuda.synchronize()
         del src, dst
-    torch.cuda.synchronize()
+
     with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
-            step()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_gpu = ev0.elapsed_time(ev1) / args.steps
-    ms_wall = wall * 1e3 / args.steps
-    tflops = flops / (ms_wall * 1e-3) / 1e12
-    achieved = flops / (ms_gpu * 1e-3) / 1e12
-
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic()}
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, args.cpu_seconds)
-        cpu["value"] = float(f"{cpu['value']:.4g}")
-
-    line = {
-        "metric": "attention fwd TFLOPs/s (4\u00b7B\u00b7H\u00b7N\u00b2\u00b7d, \u00bd if causal) and % of MI355X MFMA peak",
-        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_wall, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w["name"], "B": w["B"], "N": w["N"], "H": w["H"], "d": w["d"],
-                   "causal": w["causal"], "global_batch": w["B"], "seq_len": w["N"],
-                   "pct_of_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2), "parallelism": "single GPU"},
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(line), flush=True)
+        if args.workload == "mha16k":
+            name = "mha_n16384_b1_h16_d128"
+            out = [run_16bit(args, name, si.CONFIGS[name](), dev, stream, traffic=measured_traffic(), cpu=True)]
+        elif args.workload == "sweep":
+            out = [run_16bit(args, n, si.CONFIGS[n](), dev, stream)
+                   for n in si.CONFIGS if n.startswith("mha_n")]
+        elif args.workload == "causal":
+            out = [run_16bit(args, n, si.CONFIGS[n](), dev, stream) for n in si.CONFIGS if n.startswith("causal")]
+        elif args.workload == "varlen":
+            n = "gqa_varlen_causal_hq32_hkv8_d128"
+            out = [run_16bit(args, n, si.CONFIGS[n](), dev, stream)]
+        else:
+            out = [run_fp8(args, dev, stream)]
+    for o in out:
+        print(json.dumps(o), flush=True)
 
 
 if __name__ == "__main__":
