@@ -171,12 +171,7 @@ __global__ __launch_bounds__(256) void fp8_prepare_kernel(PrepTensor t0, PrepTen
 // Attention on e4m3 inputs
 // ============================================================================================
 
-constexpr int kThreads = 256;
-constexpr int kBr = 128;  // queries per workgroup, 32 per wave
-constexpr int kD = 128;   // head dim (bytes per row of an e4m3 tile)
-constexpr int kBc = 64;   // keys per tile = one scale block
-constexpr int kTile = kBc * kD;      // bytes of one K or V tile
-constexpr int kNI = kTile / 1024 / 4;  // 1 KB copies per wave per tensor
+constexpr int kD = 128;  // head dim (bytes per row of an e4m3 tile)
 
 // LDS tile layout: blocks of 16 rows, chunk-major inside a block (16-byte chunks), rows inside
 // a chunk column XOR-ed with 4*(chunk & 1).  Conflict free for 16-lane b128 reads of one chunk
@@ -223,12 +218,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-__global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
+// WAVES waves of 32 queries per workgroup; BC keys per tile (64 or 128, a multiple of the
+// 64-token scale block).
+template <int WAVES, int BC>
+__global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 3 : 1)) void fwd_fp8_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
     const float* __restrict__ qs, const float* __restrict__ ks_, const float* __restrict__ vs_,
     uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int N, float alpha, int num_qblocks) {
-  __shared__ __attribute__((aligned(1024))) char st0[2 * kTile];
-  __shared__ __attribute__((aligned(1024))) char st1[2 * kTile];
+  constexpr int BR = 32 * WAVES;        // queries per workgroup
+  constexpr int TILE = BC * kD;         // bytes of one K or V tile
+  constexpr int NI = TILE / 1024 / WAVES;  // 1 KB copies per wave per tensor
+  constexpr int NB_C = BC / 32;         // 32-key score blocks per tile
+  constexpr int KS = BC / 64;           // 64-key k-steps of the second product
+  static_assert(BC % 64 == 0 && NI >= 1 && NI * WAVES * 1024 == TILE, "tile shape");
+  __shared__ __attribute__((aligned(1024))) char st0[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) char st1[2 * TILE];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -241,7 +245,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   const int bh = logical / num_qblocks;
   const int h = bh % Hq, b = bh / Hq;
   const int n = N, seq_start = b * N;
-  const int q0 = qb * kBr;
+  const int q0 = qb * BR;
   const int g = h / (Hq / Hkv);
   const int qw = q0 + wave * 32;
   const int qi = qw + l32;
@@ -264,20 +268,20 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   const float* vsc = vs_ + ((int64_t)b * Hkv + g) * nblk;
 
   const int rowbytes = Hkv * kD;
-  int voff[kNI];
+  int voff[NI];
 #pragma unroll
-  for (int i = 0; i < kNI; ++i) {
+  for (int i = 0; i < NI; ++i) {
     int row, chunk;
-    f8_tile_row_chunk((wave * kNI + i) * 64 + lane, row, chunk);
+    f8_tile_row_chunk((wave * NI + i) * 64 + lane, row, chunk);
     voff[i] = row * rowbytes + chunk * 16;
   }
   const char* kbase = reinterpret_cast<const char*>(k) + ((int64_t)seq_start * Hkv + g) * kD;
   const char* vbase = reinterpret_cast<const char*>(v) + ((int64_t)seq_start * Hkv + g) * kD;
   const int nbytes = (n - 1) * rowbytes + kD;
   auto issue_tile = [&](char* stage, int tile) {
-    const int off = tile * kBc * rowbytes;
-    copy_rows_to_lds8<kNI>(kbase + off, nbytes - off, stage + wave * kNI * 1024, voff);
-    copy_rows_to_lds8<kNI>(vbase + off, nbytes - off, stage + kTile + wave * kNI * 1024, voff);
+    const int off = tile * BC * rowbytes;
+    copy_rows_to_lds8<NI>(kbase + off, nbytes - off, stage + wave * NI * 1024, voff);
+    copy_rows_to_lds8<NI>(vbase + off, nbytes - off, stage + TILE + wave * NI * 1024, voff);
   };
 
   // K operand: row 32*cb + l32, chunks 4*st + 2*hi + e (e = 0, 1)
@@ -285,7 +289,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
 #pragma unroll
   for (int e = 0; e < 2; ++e) koff[e] = 16 * ((l32 >> 4) * 128 + (2 * hi + e) * 16 + ((lane & 15) ^ (4 * e)));
   // V operand by transpose reads: lane 16G + 2r + c reads 8 bytes (half c) of row
-  // 16u + 4*(G/2) + 8*(r/4) + r%4, chunk 2*db + (G%2)
+  // 64*ks + 16u + 4*(G/2) + 8*(r/4) + r%4, chunk 2*db + (G%2)
   int vtoff;
   {
     const int G = lane >> 4, r = (lane >> 1) & 7, c = lane & 1;
@@ -299,17 +303,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   float m = -INFINITY;
   float l = 0.f;
   const float c = alpha * kLog2e;
-  const int ntiles = (n + kBc - 1) / kBc;
+  const int ntiles = (n + BC - 1) / BC;
 
   auto compute_tile = [&](const char* stage, int j) {
     const char* kt = stage;
-    const char* vt = stage + kTile;
-    const int k0 = j * kBc;
-    const int sk = e8m0_of(ksc[j]);
-    const int sv = e8m0_of(vsc[j]);
-    f32x16 s[2];
+    const char* vt = stage + TILE;
+    const int k0 = j * BC;
+    f32x16 s[NB_C];
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < NB_C; ++cb) {
+      const int sk = e8m0_of(ksc[(k0 >> 6) + (cb >> 1)]);
       s[cb] = f32x16{};
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -319,16 +322,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
         s[cb] = mma_f8(a, qf[st], s[cb], sk, sq);
       }
     }
-    if (k0 + kBc > n) {
+    if (k0 + BC > n) {
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+      for (int cb = 0; cb < NB_C; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (k0 + cb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3) >= n) s[cb][r] = -INFINITY;
     }
     float mt = -INFINITY;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < NB_C; ++cb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[cb][r]);
     mt = halves_max(mt);
@@ -346,7 +349,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
     const float mc = ((m == -INFINITY) ? 0.f : m * c) - 8.f;
     float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < NB_C; ++cb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cb][r], c, -mc));
@@ -354,24 +357,29 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
         if (r & 1) rs1 += p; else rs0 += p;
       }
     l += rs0 + rs1;
-    // P'^T as the B operand: byte 16*cb + r holds accumulator register r of block cb
-    i32x8 pf;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const int cb = w >> 2, r0 = 4 * (w & 3);
-      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[cb][r0], s[cb][r0 + 1], 0, false);
-      pf[w] = __builtin_amdgcn_cvt_pk_fp8_f32(s[cb][r0 + 2], s[cb][r0 + 3], lo, true);
-    }
+    for (int kk = 0; kk < KS; ++kk) {
+      // P'^T as the B operand of k-step kk: byte 16*cb' + r holds register r of block 2*kk + cb'
+      i32x8 pf;
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      i32x8 a;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const i32x2 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i32x2, vt + vtoff + u * 2048 + db * 512));
-        a[2 * u] = t[0];
-        a[2 * u + 1] = t[1];
+      for (int w = 0; w < 8; ++w) {
+        const int cb = 2 * kk + (w >> 2), r0 = 4 * (w & 3);
+        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[cb][r0], s[cb][r0 + 1], 0, false);
+        pf[w] = __builtin_amdgcn_cvt_pk_fp8_f32(s[cb][r0 + 2], s[cb][r0 + 3], lo, true);
       }
-      oacc[db] = mma_f8(a, pf, oacc[db], sv, 127);
+      const int sv = e8m0_of(vsc[(k0 >> 6) + kk]);
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        i32x8 a;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const i32x2 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+              LDS_PTR(i32x2, vt + vtoff + kk * 8192 + u * 2048 + db * 512));
+          a[2 * u] = t[0];
+          a[2 * u + 1] = t[1];
+        }
+        oacc[db] = mma_f8(a, pf, oacc[db], sv, 127);
+      }
     }
   };
 
@@ -409,6 +417,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_fp8_kernel(
   }
 }
 
+#ifndef ATTN_FP8_SHAPE
+#define ATTN_FP8_SHAPE 4, 64
+#endif
+
 }  // namespace
 
 hipError_t launch_fp8_prepare(const PrepareArgs& a, hipStream_t stream) {
@@ -425,10 +437,12 @@ hipError_t launch_fp8_prepare(const PrepareArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream) {
-  const int nqb = (a.N + kBr - 1) / kBr;
+  constexpr int kWaves = [] { int w[] = {ATTN_FP8_SHAPE}; return w[0]; }();
+  const int br = 32 * kWaves;
+  const int nqb = (a.N + br - 1) / br;
   const long long grid = (long long)nqb * a.Hq * a.B;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(fwd_fp8_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((fwd_fp8_kernel<ATTN_FP8_SHAPE>), dim3((unsigned)grid), dim3(64 * kWaves), 0, stream,
                      static_cast<const uint8_t*>(a.q), static_cast<const uint8_t*>(a.k),
                      static_cast<const uint8_t*>(a.v), a.q_scale, a.k_scale, a.v_scale,
                      static_cast<uint16_t*>(a.o), a.lse, a.Hq, a.Hkv, a.N, a.alpha, nqb);
