@@ -38,22 +38,29 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOPs/s (4·B·H·N²·d, ½ if causal) and % of MI355X MFMA peak"
 PEAK = {"bf16": 2516.6, "fp8": 5033.2}  # dense MFMA TFLOP/s: 256 CU x (4096 | 8192) FLOP/clk x 2.4 GHz
 HBM_PEAK_GBS = 8000.0
-# HBM-side bytes per launch of the attention kernel from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE,
-# scaled by the counters of a copy kernel of known size (profiles/fwd_bf16_d128_n16384_traffic.md).
-# Valid only for the kernel source they were taken on; any other version reports null.
-MEASURED_TRAFFIC = {"kernel_source": "exact_attention_76_amd/csrc/attn_fwd.hip",
-                    "sha256_prefix": "21e9df9fc4856c3e", "bytes": 403843800}
+# HBM-side bytes per launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, each scaled by what the
+# same counter reads for a copy kernel of known size (profiles/*_traffic.md).  An entry is valid
+# only for the kernel source it was taken on; any other version reports null.
+MEASURED_TRAFFIC = {
+    "bf16_mha16k": {"kernel_source": "exact_attention_76_amd/csrc/attn_fwd.hip",
+                    "sha256_prefix": "f62020df7fb1f8c7", "bytes": 404197568},
+    "fp8_attention": {"kernel_source": "exact_attention_76_amd/csrc/fp8.hip",
+                      "sha256_prefix": "4632dbcd9036336b", "bytes": 185523367},
+    "fp8_prepare": {"kernel_source": "exact_attention_76_amd/csrc/fp8.hip",
+                    "sha256_prefix": "4632dbcd9036336b", "bytes": 302652001},
+}
 
 
-def measured_traffic():
+def measured_traffic(key):
     import hashlib
 
-    path = os.path.join(ROOT, MEASURED_TRAFFIC["kernel_source"])
+    entry = MEASURED_TRAFFIC[key]
+    path = os.path.join(ROOT, entry["kernel_source"])
     try:
         digest = hashlib.sha256(open(path, "rb").read()).hexdigest()
     except OSError:
         return None
-    return MEASURED_TRAFFIC["bytes"] if digest.startswith(MEASURED_TRAFFIC["sha256_prefix"]) else None
+    return entry["bytes"] if digest.startswith(entry["sha256_prefix"]) else None
 
 
 def parse():
@@ -193,9 +200,10 @@ def run_fp8(args, dev, stream):
              "prepare_roofline": {"bound": "hbm", "achieved": round(prep_bytes / (pg * 1e-3) / 1e9, 1),
                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                   "frac": round(prep_bytes / (pg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                  "traffic": None, "bytes_per_launch": prep_bytes},
+                                  "traffic": measured_traffic("fp8_prepare"), "bytes_per_launch": prep_bytes},
              "prepare_plus_attention_tflops": round(inp.flops() / ((pw + ms_wall) * 1e-3) / 1e12, 2)}
-    return line(args, "fp8_b2_h16_n8192_d128", inp, inp.flops(), ms_wall, ms_gpu, "fp8", extra=extra)
+    return line(args, "fp8_b2_h16_n8192_d128", inp, inp.flops(), ms_wall, ms_gpu, "fp8", extra=extra,
+                traffic=measured_traffic("fp8_attention"))
 
 
 def main():
@@ -222,7 +230,7 @@ def main():
     with torch.cuda.stream(stream):
         if args.workload == "mha16k":
             name = "mha_n16384_b1_h16_d128"
-            out = [run_16bit(args, name, si.CONFIGS[name](), dev, stream, traffic=measured_traffic(), cpu=True)]
+            out = [run_16bit(args, name, si.CONFIGS[name](), dev, stream, traffic=measured_traffic("bf16_mha16k"), cpu=True)]
         elif args.workload == "sweep":
             out = [run_16bit(args, n, si.CONFIGS[n](), dev, stream)
                    for n in si.CONFIGS if n.startswith("mha_n")]
