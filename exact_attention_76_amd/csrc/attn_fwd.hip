@@ -27,6 +27,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace attn {
@@ -146,11 +148,21 @@ __device__ __forceinline__ void copy_rows_to_lds(const char* base, int nbytes, c
 //   WAVES     waves per workgroup, 32 queries each (the workgroup owns 32 * WAVES queries);
 //   EXPFIRST  take all exponentials of a tile before its second product, instead of one
 //             k-step at a time next to that k-step's products.
-template <int WAVES_, bool EXPFIRST_>
+//   PP        ping-pong: the waves of the two halves of the workgroup (one of each per SIMD)
+//             run one phase apart, so that one half's products and the other half's softmax
+//             occupy a SIMD at the same time (see the main loop).
+//   PD        (ping-pong only) how many products ahead the LDS operand reads are issued.
+template <int WAVES_, bool EXPFIRST_, bool PP_ = false, int PD_ = 4>
 struct LoopShape {
   static constexpr int WAVES = WAVES_;
   static constexpr bool EXPFIRST = EXPFIRST_;
+  static constexpr bool PP = PP_;
+  static constexpr int PD = PD_;
 };
+
+// Workgroup barrier between ping-pong phases.  The asm statement is a compiler memory barrier
+// (no LDS access moves across it); LDS reads of this wave are complete before it arrives.
+__device__ __forceinline__ void phase_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int D, int BC, typename SH, bool BF16, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
@@ -170,11 +182,15 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
   static_assert(BC % 32 == 0 && D % 32 == 0 && NI * WAVES * 1024 == TILE_BYTES && (NI % IPB == 0 || NI < IPB),
                 "tile shape");
 
-  // two K and two V tile buffers; separate objects so the compiler can tell them apart
+  // two (ping-pong: three) K and V tile buffers; separate objects so the compiler can tell
+  // them apart
+  constexpr int NBUF = SH::PP ? 3 : 2;
   __shared__ __attribute__((aligned(1024))) char kb0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char kb1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kb2[NBUF > 2 ? TILE_BYTES : 1];
   __shared__ __attribute__((aligned(1024))) char vb0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char vb1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vb2[NBUF > 2 ? TILE_BYTES : 1];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -260,10 +276,8 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
   const int kv_end = CAUSAL ? min(n, q0 + BR) : n;
   const int ntiles = (kv_end + BC - 1) / BC;
 
-  auto compute_tile = [&](const char* ks, const char* vs, int j) {
-    const int k0 = j * BC;
-    // S^T = K Q^T: lane holds query qi, keys k0 + 32*cb + 8*(r/4) + 4*hi + r%4
-    f32x16 s[NB_C];
+  // S^T = K Q^T: lane holds query qi, keys k0 + 32*cb + 8*(r/4) + 4*hi + r%4
+  auto gemm1 = [&](const char* ks, f32x16* s) {
 #pragma unroll
     for (int cb = 0; cb < NB_C; ++cb) {
       s[cb] = f32x16{};
@@ -273,6 +287,10 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
         s[cb] = mma32<BF16>(a, qf[st], s[cb]);
       }
     }
+  };
+  // Mask, running maximum and lazy rescale of tile j; returns the stabiliser m*c.
+  auto update_max = [&](f32x16* s, int j) -> float {
+    const int k0 = j * BC;
     const bool need_mask = (k0 + BC > n) || (CAUSAL && k0 + BC - 1 > qw);
     if (need_mask) {
 #pragma unroll
@@ -300,7 +318,24 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
 #pragma unroll
       for (int db = 0; db < NB_D; ++db) oacc[db] *= corr;
     }
-    const float mc = (m == -INFINITY) ? 0.f : m * c;
+    return (m == -INFINITY) ? 0.f : m * c;
+  };
+  // O^T += V^T P^T for one k-step (16 keys): accumulator registers 8*(st%2) .. +7 of block st/2
+  auto gemm2_step = [&](const char* vs, int st, u32x4 pf) {
+#pragma unroll
+    for (int db = 0; db < NB_D; ++db) {
+      const int imm = st * 256 * NCH + db * 1024;
+      const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vs + vtoff[0] + imm));
+      const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vs + vtoff[1] + imm));
+      const u32x2 a0 = __builtin_bit_cast(u32x2, t0), a1 = __builtin_bit_cast(u32x2, t1);
+      oacc[db] = mma32<BF16>(u32x4{a0[0], a0[1], a1[0], a1[1]}, pf, oacc[db]);
+    }
+  };
+
+  auto compute_tile = [&](const char* ks, const char* vs, int j) {
+    f32x16 s[NB_C];
+    gemm1(ks, s);
+    const float mc = update_max(s, j);
     float rs0 = 0.f, rs1 = 0.f;
     if constexpr (SH::EXPFIRST) {
 #pragma unroll
@@ -312,7 +347,6 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
           if (r & 1) rs1 += p; else rs0 += p;
         }
     }
-    // O^T += V^T P^T; k-step st takes accumulator registers 8*(st%2) .. +7 of block st/2
 #pragma unroll
     for (int st = 0; st < KS_C; ++st) {
       const int cb = st >> 1, base = (st & 1) * 8;
@@ -326,34 +360,170 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
           if (t & 1) rs1 += p[t]; else rs0 += p[t];
         }
       }
-      const u32x4 pf = u32x4{pack2<BF16>(p[0], p[1]), pack2<BF16>(p[2], p[3]), pack2<BF16>(p[4], p[5]),
-                             pack2<BF16>(p[6], p[7])};
-#pragma unroll
-      for (int db = 0; db < NB_D; ++db) {
-        const int imm = st * 256 * NCH + db * 1024;
-        const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vs + vtoff[0] + imm));
-        const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vs + vtoff[1] + imm));
-        const u32x2 a0 = __builtin_bit_cast(u32x2, t0), a1 = __builtin_bit_cast(u32x2, t1);
-        oacc[db] = mma32<BF16>(u32x4{a0[0], a0[1], a1[0], a1[1]}, pf, oacc[db]);
-      }
+      gemm2_step(vs, st, u32x4{pack2<BF16>(p[0], p[1]), pack2<BF16>(p[2], p[3]), pack2<BF16>(p[4], p[5]),
+                               pack2<BF16>(p[6], p[7])});
     }
     l += rs0 + rs1;
   };
 
-  // ---- main loop: two buffer pairs, unrolled by two so each half names its buffers ----
-  issue_tile(kb0, vb0, 0);
-  __builtin_amdgcn_s_waitcnt(0);  // Q fragments and tile 0 have arrived
-  __syncthreads();
-  for (int j = 0; j < ntiles; j += 2) {
-    if (j + 1 < ntiles) issue_tile(kb1, vb1, j + 1);
-    if (!CAUSAL || j * BC <= qw + 31) compute_tile(kb0, vb0, j);
-    __builtin_amdgcn_s_waitcnt(0);
+  if constexpr (!SH::PP) {
+    // ---- main loop: two buffer pairs, unrolled by two so each half names its buffers ----
+    issue_tile(kb0, vb0, 0);
+    __builtin_amdgcn_s_waitcnt(0);  // Q fragments and tile 0 have arrived
     __syncthreads();
-    if (j + 1 >= ntiles) break;
-    if (j + 2 < ntiles) issue_tile(kb0, vb0, j + 2);
-    if (!CAUSAL || (j + 1) * BC <= qw + 31) compute_tile(kb1, vb1, j + 1);
-    __builtin_amdgcn_s_waitcnt(0);
+    for (int j = 0; j < ntiles; j += 2) {
+      if (j + 1 < ntiles) issue_tile(kb1, vb1, j + 1);
+      if (!CAUSAL || j * BC <= qw + 31) compute_tile(kb0, vb0, j);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (j + 1 >= ntiles) break;
+      if (j + 2 < ntiles) issue_tile(kb0, vb0, j + 2);
+      if (!CAUSAL || (j + 1) * BC <= qw + 31) compute_tile(kb1, vb1, j + 1);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  } else {
+    // ---- ping-pong main loop ----
+    // Every wave runs the phases M_0 V_0 M_1 V_1 ... M_J (J tiles): M_j multiplies P_{j-1} by
+    // V_{j-1} (second product of the previous tile) and forms S_j = K_j Q^T; V_j takes the
+    // softmax of S_j into the packed P_j.  A barrier ends every phase.  The second half of the
+    // workgroup (waves HW..) passes one extra barrier at the start, so it runs one phase behind
+    // the first half: while one wave of a SIMD multiplies, the other takes exponentials.
+    // Barrier step t holds phase t of the first half and phase t-1 of the second half.
+    // Tiles rotate through three K and three V buffers (tile j in kb[j%3], vb[j%3]).  In its
+    // phase V_j the first half copies K_{j+2} (step 2j+1) and the second half copies V_{j+1}
+    // (step 2j+2); both buffers were last read in the phases M_{j-1} (steps 2j-2, 2j-1).  Each
+    // half waits for its copies at the end of its next M phase (steps 2j+2 and 2j+3); both
+    // tiles are first read in the first half's M_{j+2}, at step 2j+4.
+    constexpr int HW = WAVES / 2;
+    constexpr int NIB = TILE_BYTES / 1024 / HW;  // copies per wave per tile
+    static_assert(NIB * HW * 1024 == TILE_BYTES && (NIB % IPB == 0 || NIB < IPB), "copy split");
+    const bool second = wave >= HW;
+    const int wb = wave % HW;
+    int voffb;
+    {
+      int row, chunk;
+      tile_row_chunk<D>(wb * NIB * 64 + lane, row, chunk);
+      voffb = row * rowbytes + chunk * 16;
+    }
+    // copies of this wave's part of one tile; a tile past the end reads as zero
+    auto copy = [&](const char* base, char* dst, int tile) {
+      const int64_t off = (int64_t)tile * BC * rowbytes;
+      const int rem = off < nbytes ? (int)(nbytes - off) : 0;
+      copy_rows_to_lds<NIB, IPB>(base + (rem ? off : 0), rem, dst + wb * NIB * 1024, voffb, blk_bytes);
+    };
+    const int jw = CAUSAL ? min(ntiles, (qw + 31) / BC + 1) : ntiles;  // tiles this wave needs
+    f32x16 s[NB_C];
+    u32x4 pf[KS_C];
+    // An M phase is one stream of products (the second product of the previous tile, then the
+    // first product of this tile) whose LDS operands are read PD products ahead.
+    constexpr int N2 = KS_C * NB_D, N1 = NB_C * KS_D, PD = SH::PD;
+    auto operand = [&](const char* ks, const char* vs, int i) -> u32x4 {
+      if (i < N2) {
+        const int st = i / NB_D, db = i % NB_D;
+        const int imm = st * 256 * NCH + db * 1024;
+        const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vs + vtoff[0] + imm));
+        const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, vs + vtoff[1] + imm));
+        const u32x2 a0 = __builtin_bit_cast(u32x2, t0), a1 = __builtin_bit_cast(u32x2, t1);
+        return u32x4{a0[0], a0[1], a1[0], a1[1]};
+      }
+      const int cb = (i - N2) / KS_D, st = (i - N2) % KS_D;
+      return *reinterpret_cast<const u32x4*>(ks + koff[st & 1] + cb * 512 * NCH + 512 * (st & ~1));
+    };
+    auto product = [&](int i, u32x4 a) {
+      if (i < N2) {
+        const int st = i / NB_D, db = i % NB_D;
+        oacc[db] = mma32<BF16>(a, pf[st], oacc[db]);
+      } else {
+        const int cb = (i - N2) / KS_D, st = (i - N2) % KS_D;
+        if (st == 0) s[cb] = f32x16{};
+        s[cb] = mma32<BF16>(a, qf[st], s[cb]);
+      }
+    };
+    // Every M phase up to this wave's last tile runs the whole stream: in M_0 P is zero and
+    // the V buffer holds a copy of V_0 (finite values), so the second product adds exact
+    // zeros; in M_jw the first product is formed and not used.
+    auto mphase = [&](const char* ks, const char* vs, int j) {
+      if (j <= jw) {
+        u32x4 win[PD];
+#pragma unroll
+        for (int i = 0; i < PD; ++i) win[i] = operand(ks, vs, i);
+#pragma unroll
+        for (int i = 0; i < N2 + N1; ++i) {
+          const u32x4 a = win[i % PD];
+          if (i + PD < N2 + N1) win[i % PD] = operand(ks, vs, i + PD);
+          product(i, a);
+        }
+        // keep that order through instruction scheduling: the reads of the first PD operands,
+        // then per product: the product, the reads of the operand PD places ahead (a V^T
+        // operand is two LDS reads, a K operand one)
+        auto reads = [](int i) {
+          if (i < N2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        };
+#pragma unroll
+        for (int i = 0; i < PD; ++i) reads(i);
+#pragma unroll
+        for (int i = 0; i < N2 + N1; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (i + PD < N2 + N1) reads(i + PD);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's copies (issued in the last V phase) have landed
+    };
+    // V phase: softmax of S_j into P_j; the copies of this phase are spread over it
+    auto vphase = [&](char* kdst, char* vdst, int j) {
+      if (!second) copy(kbase, kdst, j + 2);
+      else copy(vbase, vdst, j + 1);
+      if (j < jw) {
+        const float mc = update_max(s, j);
+        float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+        for (int st = 0; st < KS_C; ++st) {
+          const int cb = st >> 1, base = (st & 1) * 8;
+          float p[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cb][base + t], c, -mc));
+            if (t & 1) rs1 += p[t]; else rs0 += p[t];
+          }
+          pf[st] = u32x4{pack2<BF16>(p[0], p[1]), pack2<BF16>(p[2], p[3]), pack2<BF16>(p[4], p[5]),
+                         pack2<BF16>(p[6], p[7])};
+        }
+        l += rs0 + rs1;
+      }
+    };
+    if (!second) {
+      copy(kbase, kb0, 0);
+      copy(kbase, kb1, 1);
+    } else {
+      copy(vbase, vb0, 0);
+      copy(vbase, vb2, 0);  // read (times P = 0) by M_0
+    }
+#pragma unroll
+    for (int st = 0; st < KS_C; ++st) pf[st] = u32x4{0, 0, 0, 0};
+    __builtin_amdgcn_s_waitcnt(0);  // Q fragments and tiles K_0, K_1, V_0 have arrived
     __syncthreads();
+    if (second) phase_barrier();
+    for (int j = 0;; j += 3) {
+      mphase(kb0, vb2, j);
+      phase_barrier();
+      if (j == ntiles) break;
+      vphase(kb2, vb1, j);
+      phase_barrier();
+      mphase(kb1, vb0, j + 1);
+      phase_barrier();
+      if (j + 1 == ntiles) break;
+      vphase(kb0, vb2, j + 1);
+      phase_barrier();
+      mphase(kb2, vb1, j + 2);
+      phase_barrier();
+      if (j + 2 == ntiles) break;
+      vphase(kb1, vb0, j + 2);
+      phase_barrier();
+    }
+    // the first half passes one barrier fewer in the loop; it joins the second half's last
+    // barrier after its epilogue (below)
   }
 
   // ---- epilogue: O / l, L = alpha*m + ln l ----
@@ -376,6 +546,9 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
       else idx = ((int64_t)b * Hq + h) * N + qi;
       lse[idx] = L;
     }
+  }
+  if constexpr (SH::PP) {
+    if (wave < WAVES / 2) phase_barrier();
   }
 }
 
@@ -401,17 +574,18 @@ hipError_t launch_modes(const FwdArgs& a, hipStream_t stream) {
 }
 
 // Per head dim: keys per tile and loop shape.  Eight waves (256 queries) per workgroup, one
-// workgroup per CU: the K/V tile copies (which compete with the operand reads for LDS
-// bandwidth) are shared by twice as many waves as with four-wave workgroups; measured on
-// MI355X this is 8-13% faster for every head dim.
+// workgroup per CU: the K/V tile copies are shared by all eight waves.  d = 128 and d = 256 run
+// the ping-pong loop (measured on MI355X: +4-7% over the plain loop); at d = 64 the softmax
+// outweighs the products and the plain loop, which lets the two waves of a SIMD share the
+// VALU freely, is as fast.
 #ifndef ATTN_D64_SHAPE
 #define ATTN_D64_SHAPE 64, LoopShape<8, false>
 #endif
 #ifndef ATTN_D128_SHAPE
-#define ATTN_D128_SHAPE 64, LoopShape<8, true>
+#define ATTN_D128_SHAPE 64, LoopShape<8, true, true, 3>
 #endif
 #ifndef ATTN_D256_SHAPE
-#define ATTN_D256_SHAPE 32, LoopShape<8, false>
+#define ATTN_D256_SHAPE 32, LoopShape<8, false, true, 4>
 #endif
 
 template <bool BF16>
