@@ -88,6 +88,46 @@ __device__ __forceinline__ int xcd_remap(int wg, int total) {
   return x * q + (x < r ? x : r) + i;
 }
 
+// Work decomposition: hardware workgroup id -> (query block, head, sequence).  Workgroups are
+// dispatched round-robin over the 8 XCDs (id mod 8), each XCD running its share in id order.
+// When the heads split evenly over the XCDs, every XCD owns the same heads of every sequence,
+// so packed sequences of unequal length load all XCDs alike; whole KV groups stay on one XCD
+// (their query heads share the group's K/V in that XCD's L2) when the KV heads split evenly too.
+// Inside an XCD, causal grids run all query blocks longest first (a block's work grows with
+// its index); non-causal grids keep the blocks of one head together.  Otherwise each XCD
+// takes one contiguous range of (sequence, head, block) ids, causal blocks longest first.
+template <bool CAUSAL>
+__device__ __forceinline__ void decompose(int wg, int nqb, int Hq, int Hkv, int B, int& qb, int& h, int& b) {
+  constexpr int kXcd = 8;
+  if (Hq % kXcd == 0) {
+    const int x = wg % kXcd, slot = wg / kXcd;
+    const int hpx = Hq / kXcd;  // heads per XCD and sequence
+    int r;
+    if (CAUSAL) {
+      qb = nqb - 1 - slot / (hpx * B);
+      r = slot % (hpx * B);
+    } else {
+      qb = slot % nqb;
+      r = slot / nqb;
+    }
+    b = r / hpx;
+    const int hh = r % hpx;
+    if (Hkv % kXcd == 0) {
+      const int G = Hq / Hkv;  // query heads per KV group; groups x, x + 8, ... live on XCD x
+      h = (x + kXcd * (hh / G)) * G + hh % G;
+    } else {
+      h = x + kXcd * hh;
+    }
+  } else {
+    const int logical = xcd_remap(wg, nqb * Hq * B);
+    qb = logical % nqb;
+    const int bh = logical / nqb;
+    h = bh % Hq;
+    b = bh / Hq;
+    if (CAUSAL) qb = nqb - 1 - qb;
+  }
+}
+
 
 // ---- LDS tile layout -------------------------------------------------------------------------
 // A K or V tile of BC rows x D columns (16-bit) is stored as blocks of 16 rows; inside a block
@@ -198,11 +238,8 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
   const int l32 = lane & 31, hi = lane >> 5;
 
   // ---- which (sequence, head, query block) ----
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  int qb = logical % num_qblocks;
-  const int bh = logical / num_qblocks;
-  const int h = bh % Hq, b = bh / Hq;
-  if (CAUSAL) qb = num_qblocks - 1 - qb;  // longest query blocks first
+  int qb, h, b;
+  decompose<CAUSAL>(blockIdx.x, num_qblocks, Hq, Hkv, nseq, qb, h, b);
   int seq_start, n;
   if constexpr (VARLEN) {
     seq_start = cu_seqlens[b];
