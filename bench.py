@@ -11,6 +11,10 @@ non-causal figure at 16k).  ``--workload`` selects the other measured configurat
   varlen  bf16 causal GQA (Hq=32, Hkv=8, d=128), 8 packed sequences of 256..8192 tokens
   fp8     e4m3 non-causal B=2 H=16 N=8192 d=128 on pre-quantised inputs; the FP8 pre-pass
           (Hadamard rotation + block quantisation, HBM-bound) is timed separately
+  ceiling the matrix-core ceiling the attention kernels run against: back-to-back
+          v_mfma_f32_32x32x16_bf16 on random operands on every CU (2 and 4 waves per SIMD),
+          with no LDS or vector-ALU work; under the chip's power limit this sits well below
+          the nominal dense peak
 
 Metric (FlashAttention-3 digest, section 7.1): TFLOPs/s with FLOPs = 4 * B * H * N^2 * d
 (halved when causal; summed per sequence for packed inputs), and the fraction of MI355X dense
@@ -43,11 +47,11 @@ HBM_PEAK_GBS = 8000.0
 # only for the kernel source it was taken on; any other version reports null.
 MEASURED_TRAFFIC = {
     "bf16_mha16k": {"kernel_source": "exact_attention_76_amd/csrc/attn_fwd.hip",
-                    "sha256_prefix": "f62020df7fb1f8c7", "bytes": 404197568},
+                    "sha256_prefix": "0572094c757f9ad2", "bytes": 404332430},
     "fp8_attention": {"kernel_source": "exact_attention_76_amd/csrc/fp8.hip",
-                      "sha256_prefix": "4632dbcd9036336b", "bytes": 185523367},
+                      "sha256_prefix": "77fa239ce4149371", "bytes": 185607647},
     "fp8_prepare": {"kernel_source": "exact_attention_76_amd/csrc/fp8.hip",
-                    "sha256_prefix": "4632dbcd9036336b", "bytes": 302652001},
+                    "sha256_prefix": "77fa239ce4149371", "bytes": 302675418},
 }
 
 
@@ -68,7 +72,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="mha16k", choices=["mha16k", "sweep", "causal", "varlen", "fp8"])
+    ap.add_argument("--workload", default="mha16k", choices=["mha16k", "sweep", "causal", "varlen", "fp8", "ceiling"])
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -206,6 +210,45 @@ def run_fp8(args, dev, stream):
                 traffic=measured_traffic("fp8_attention"))
 
 
+def run_ceiling(args, dev, stream):
+    import ctypes
+
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "exact_attention_76_amd", "libceiling.so"))
+    lib.ceiling_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    src = torch.randn(65536 * 8, device=dev, generator=gen).to(torch.bfloat16)  # 65536 operands of 8 bf16
+    iters = 4000
+    out = []
+    for waves_per_simd, grid in ((2, 512), (4, 1024)):
+        sink = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+
+        def step():
+            rc = lib.ceiling_mfma_bf16(src.data_ptr(), sink.data_ptr(), iters, grid, stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"ceiling_mfma_bf16 failed with hipError {rc}")
+
+        steps, warmup = max(1, min(args.steps, 10)), max(1, min(args.warmup, 5))
+        ms_wall, ms_gpu = timed(step, stream, steps, warmup)
+        flops = grid * 4 * iters * 8 * (32 * 32 * 16 * 2)
+        achieved = flops / (ms_gpu * 1e-3) / 1e12
+        out.append({
+            "metric": "sustained v_mfma_f32_32x32x16_bf16 throughput on random operands (matrix-core ceiling)",
+            "value": round(flops / (ms_wall * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
+            "warmup": warmup, "ms_per_step": round(ms_wall, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"mfma_bf16_ceiling_{waves_per_simd}_waves_per_simd", "workgroups": grid,
+                       "waves_per_simd": waves_per_simd, "instructions_per_wave": 8 * iters,
+                       "pct_of_peak": round(100 * achieved / PEAK["bf16"], 2), "parallelism": "single GPU"},
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK["bf16"], "unit": "TFLOP/s",
+                         "frac": round(achieved / PEAK["bf16"], 4), "traffic": None},
+            "cpu_baseline": None,
+        })
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -239,8 +282,10 @@ def main():
         elif args.workload == "varlen":
             n = "gqa_varlen_causal_hq32_hkv8_d128"
             out = [run_16bit(args, n, si.CONFIGS[n](), dev, stream)]
-        else:
+        elif args.workload == "fp8":
             out = [run_fp8(args, dev, stream)]
+        else:
+            out = run_ceiling(args, dev, stream)
     for o in out:
         print(json.dumps(o), flush=True)
 

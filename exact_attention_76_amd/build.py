@@ -1,4 +1,5 @@
-"""Build libattn.so (all HIP sources under csrc/) for gfx950 with hipcc."""
+"""Build libattn.so (the attention path: api, attn_fwd, fp8) and libceiling.so (the matrix-core
+throughput probe that bench.py reports beside the attention figures) for gfx950 with hipcc."""
 from __future__ import annotations
 
 import concurrent.futures
@@ -13,6 +14,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJ_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 SOURCES = ["api.hip", "attn_fwd.hip", "fp8.hip"]
+CEILING_LIB = os.path.join(PKG, "libceiling.so")
+CEILING_SOURCES = ["ceiling.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: hipcc must not form v_pk_{add,mul,fma}_f32 from scalar or float2 code.
@@ -32,14 +35,21 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build() -> str:
-    """Compile every source (in parallel) and link libattn.so in the package directory."""
-    os.makedirs(OBJ_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs: list[str], lib: str) -> None:
+    tmp = lib + ".tmp"
     subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs], check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build() -> str:
+    """Compile every source (in parallel) and link libattn.so and libceiling.so in the package
+    directory; returns the path of libattn.so."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    sources = SOURCES + CEILING_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(sources)) as ex:
+        objs = dict(zip(sources, ex.map(_compile, sources)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in CEILING_SOURCES], CEILING_LIB)
     return LIB
 
 

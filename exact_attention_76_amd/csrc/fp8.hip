@@ -11,8 +11,8 @@
 //   * Pre-pass: one workgroup per (tensor, batch, head, 64-token block); four lanes per token
 //     row hold 32 elements each; the Walsh-Hadamard butterflies run in fp64 (five stages in
 //     registers, two across the lane quad), so the rotated values are exact; the block's
-//     largest magnitude picks the exponent and every element is rounded to e4m3 in software
-//     from its exact fp64 value.
+//     largest magnitude picks the exponent and every element is rounded to e4m3 from its exact
+//     fp64 value (fp64 -> fp32 rounded to odd, then the hardware's nearest-even conversion).
 //   * Attention: the structure of the 16-bit kernel (128 queries per workgroup, scores formed
 //     transposed, online softmax in fp32, K/V tiles copied buffer-to-LDS, two LDS stages), with
 //     both products on v_mfma_scale_f32_32x32x64_f8f6f4.  The per-block power-of-two scales of
@@ -55,23 +55,16 @@ struct PrepTensor {
   int scale_shift;    // log2 of the extra divisor folded into the scale (7 for rotated K)
 };
 
-// Nearest e4m3 (OCP, "fn") code to z, ties to the even code, sign kept, |z| clamped to 448.
-__device__ __forceinline__ uint32_t e4m3_rne(double z) {
-  const uint64_t bits = (uint64_t)__double_as_longlong(z);
-  const uint32_t sign = (uint32_t)(bits >> 56) & 0x80u;
-  const double a = fabs(z);
-  if (a >= 448.0) return sign | 0x7Eu;
-  if (a < 0.015625) {  // below 2^-6: the subnormal grid, step 2^-9 (code 8 is 2^-6 itself)
-    return sign | (uint32_t)rint(a * 512.0);
-  }
-  int E = (int)((__double_as_longlong(a) >> 52) & 0x7FF) - 1023;  // floor(log2 a), -6..8
-  // a * 2^(3 - E) lies in [8, 16): the 3-bit mantissa plus the implicit bit
-  double q = rint(a * __longlong_as_double((long long)(1023 + 3 - E) << 52));
-  if (q >= 16.0) {
-    q = 8.0;
-    E += 1;
-  }
-  return sign | (uint32_t)((E + 7) << 3) | ((uint32_t)q - 8u);
+// fp64 -> fp32 rounded to odd: the value truncated toward zero, its last bit set when the
+// conversion is inexact.  Rounding to odd at fp32's 24 bits and then to nearest even at e4m3's
+// 4 bits gives the nearest-even e4m3 value of the fp64 input itself (the intermediate keeps
+// more than one extra bit), so the hardware fp32 -> e4m3 conversion can finish the job.
+__device__ __forceinline__ float f32_round_odd(double z) {
+  const float f = (float)z;
+  const double back = (double)f;
+  uint32_t fb = __float_as_uint(f);
+  if (back != z) fb = (fb - (fabs(back) > fabs(z) ? 1u : 0u)) | 1u;
+  return __uint_as_float(fb);
 }
 
 __device__ __forceinline__ double shfl_xor_d(double x, int mask) {
@@ -157,9 +150,13 @@ __global__ __launch_bounds__(256) void fp8_prepare_kernel(PrepTensor t0, PrepTen
   if (valid) {
     uint32_t w[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      w[j] = e4m3_rne(y[4 * j] * inv) | (e4m3_rne(y[4 * j + 1] * inv) << 8) | (e4m3_rne(y[4 * j + 2] * inv) << 16) |
-             (e4m3_rne(y[4 * j + 3] * inv) << 24);
+    for (int j = 0; j < 8; ++j) {
+      // |y| * 2^-e <= 448 by the choice of e, so the conversions never saturate
+      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f32_round_odd(y[4 * j] * inv), f32_round_odd(y[4 * j + 1] * inv),
+                                                     0, false);
+      w[j] = __builtin_amdgcn_cvt_pk_fp8_f32(f32_round_odd(y[4 * j + 2] * inv), f32_round_odd(y[4 * j + 3] * inv), lo,
+                                             true);
+    }
     u32x4* dst = reinterpret_cast<u32x4*>(t.x8 + rowoff * 128 + 32 * p);
     dst[0] = u32x4{w[0], w[1], w[2], w[3]};
     dst[1] = u32x4{w[4], w[5], w[6], w[7]};
