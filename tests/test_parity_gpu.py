@@ -52,6 +52,24 @@ def test_varlen_small(d, causal):
     _compare_full(inp, f"varlen small d={d} causal={causal}")
 
 
+# Head counts that take each branch of the work decomposition: heads spread over the 8 XCDs in
+# whole KV groups (Hkv a multiple of 8, groups of 1 and 3 query heads), one query head at a
+# time (Hq a multiple of 8 only), or the contiguous-range fallback (Hq not a multiple of 8);
+# odd batch, ragged multi-tile length, every element compared.
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Hq,Hkv,d", [(8, 8, 128), (24, 8, 128), (16, 4, 128), (8, 1, 256), (8, 2, 64), (12, 4, 128)])
+def test_head_splits_over_xcds(Hq, Hkv, d, causal):
+    inp = si.dense_inputs(3, 300, Hq, d, Hkv=Hkv, causal=causal, seed=700 + Hq + 3 * Hkv + d + causal)
+    _compare_full(inp, f"head split Hq={Hq} Hkv={Hkv} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(16, 4), (16, 8)])
+def test_varlen_head_splits(Hq, Hkv):
+    """Packed sequences of unequal length with the per-XCD head split (by head and by group)."""
+    inp = si.varlen_inputs([700, 33, 256, 1, 513], Hq, Hkv, 128, causal=True, seed=800 + Hq + Hkv)
+    _compare_full(inp, f"varlen head split Hq={Hq} Hkv={Hkv}")
+
+
 def test_varlen_max_seqlen_above_longest():
     """N larger than every sequence only grows the grid; extra blocks exit."""
     inp = si.varlen_inputs([5, 130], 2, 2, 128, causal=True, seed=300)
