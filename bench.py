@@ -24,7 +24,9 @@ Each line carries
   roofline     -- algorithmic FLOPs per launch over the kernel's mean launch time, measured
                   with HIP events on the stream the kernel runs on, against the dtype's peak;
   cpu_baseline -- (headline only) the fp64 CPU oracle timed on a bounded sample of query rows
-                  of the same workload, as attention-FLOP throughput.
+                  of the same workload, as attention-FLOP throughput;
+and, in config, the median and best single launch from a second pass of the same K launches
+with an event pair around each (after the timed region, so it does not perturb it).
 """
 from __future__ import annotations
 
@@ -103,7 +105,7 @@ def cpu_baseline(inp, target_s: float) -> dict:
         if el >= target_s or el >= 30.0:
             break
     return {"value": float(f"{flops / el / 1e12:.4g}"), "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{rows} random (head, query) rows of the same workload, all keys each, fp64, {el:.1f} s"}
 
 
@@ -127,6 +129,32 @@ def timed(step, stream, steps, warmup):
     return wall, ev0.elapsed_time(ev1) / steps
 
 
+def per_launch(step, stream, steps):
+    """After the timed region: the same launches again, each between two events on ``stream``.
+    Returns (median ms, min ms) per launch."""
+    import torch
+
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)])
+    return float(np.median(ms)), float(ms.min())
+
+
+def cpu_model() -> str:
+    try:
+        for line_ in open("/proc/cpuinfo"):
+            if line_.startswith("model name"):
+                return line_.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def to_dev(bits, dtype, dev):
     import torch
 
@@ -134,13 +162,18 @@ def to_dev(bits, dtype, dev):
     return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16).to(dev)
 
 
-def line(args, name, inp, flops, ms_wall, ms_gpu, dtype, extra=None, traffic=None, cpu=None):
+def line(args, name, inp, flops, ms_wall, ms_gpu, dtype, extra=None, traffic=None, cpu=None, launches=None):
     peak = PEAK[dtype]
     tflops = flops / (ms_wall * 1e-3) / 1e12
     achieved = flops / (ms_gpu * 1e-3) / 1e12
     cfg = {"workload": name, "B": inp.B, "N": inp.N, "Hq": inp.Hq, "Hkv": inp.Hkv, "d": inp.d,
            "causal": inp.causal, "varlen": inp.cu_seqlens is not None, "tokens": inp.total_tokens,
            "flops_per_step": flops, "pct_of_peak": round(100 * tflops / peak, 2), "parallelism": "single GPU"}
+    if launches is not None:
+        med, best = launches
+        cfg.update({"ms_event_mean": round(ms_gpu, 4), "ms_launch_median": round(med, 4), "ms_launch_min": round(best, 4),
+                    "tflops_launch_median": round(flops / (med * 1e-3) / 1e12, 2),
+                    "tflops_launch_best": round(flops / (best * 1e-3) / 1e12, 2)})
     if extra:
         cfg.update(extra)
     return {
@@ -172,8 +205,10 @@ def run_16bit(args, name, inp, dev, stream, traffic=None, cpu=False):
                     max_seqlen=inp.N if cu is not None else None, stream=stream)
 
     ms_wall, ms_gpu = timed(step, stream, args.steps, args.warmup)
+    launches = per_launch(step, stream, args.steps)
     cpu_res = cpu_baseline(inp, args.cpu_seconds) if cpu and not args.no_cpu_baseline else None
-    return line(args, name, inp, inp.flops(), ms_wall, ms_gpu, inp.dtype, traffic=traffic, cpu=cpu_res)
+    return line(args, name, inp, inp.flops(), ms_wall, ms_gpu, inp.dtype, traffic=traffic, cpu=cpu_res,
+                launches=launches)
 
 
 def run_fp8(args, dev, stream):
@@ -196,6 +231,7 @@ def run_fp8(args, dev, stream):
         ea.attn_fp8_prepare(q, k, v, q8, k8, v8, qs, ks, vs, hadamard_signs=signs, stream=stream)
 
     ms_wall, ms_gpu = timed(attn, stream, args.steps, args.warmup)
+    launches = per_launch(attn, stream, args.steps)
     pw, pg = timed(prep, stream, args.steps, args.warmup)
     nblk = -(-inp.N // 64)
     prep_bytes = 3 * q.numel() * 2 + 3 * q.numel() + 3 * inp.B * inp.Hq * nblk * 4 + inp.d
@@ -207,7 +243,7 @@ def run_fp8(args, dev, stream):
                                   "traffic": measured_traffic("fp8_prepare"), "bytes_per_launch": prep_bytes},
              "prepare_plus_attention_tflops": round(inp.flops() / ((pw + ms_wall) * 1e-3) / 1e12, 2)}
     return line(args, "fp8_b2_h16_n8192_d128", inp, inp.flops(), ms_wall, ms_gpu, "fp8", extra=extra,
-                traffic=measured_traffic("fp8_attention"))
+                traffic=measured_traffic("fp8_attention"), launches=launches)
 
 
 def run_ceiling(args, dev, stream):
