@@ -21,6 +21,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -packed-fp32-ops: hipcc must not form v_pk_{add,mul,fma}_f32 from scalar or float2 code.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
+# Extra compiler arguments (whitespace-separated), e.g. a different loop shape for an ablation run:
+#   ATTN_HIPCC_EXTRA='-DATTN_D128_SHAPE=64,attn::LoopShape<8,true>' python exact_attention_76_amd/build.py
+FLAGS += os.environ.get("ATTN_HIPCC_EXTRA", "").split()
 
 
 def _compile(src: str) -> str:
