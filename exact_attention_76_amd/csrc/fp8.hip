@@ -13,9 +13,11 @@
 //     registers, two across the lane quad), so the rotated values are exact; the block's
 //     largest magnitude picks the exponent and every element is rounded to e4m3 from its exact
 //     fp64 value (fp64 -> fp32 rounded to odd, then the hardware's nearest-even conversion).
-//   * Attention: the structure of the 16-bit kernel (128 queries per workgroup, scores formed
-//     transposed, online softmax in fp32, K/V tiles copied buffer-to-LDS, two LDS stages), with
-//     both products on v_mfma_scale_f32_32x32x64_f8f6f4.  The per-block power-of-two scales of
+//   * Attention: the plain loop of the 16-bit kernel (scores formed transposed, online softmax
+//     in fp32, K/V tiles copied buffer-to-LDS, two LDS stages, one barrier per tile) with four
+//     waves (128 queries) per workgroup and three workgroups per CU -- the softmax is the larger
+//     share here, and three waves per SIMD hide it better than two in a ping-pong -- and both
+//     products on v_mfma_scale_f32_32x32x64_f8f6f4.  The per-block power-of-two scales of
 //     Q, K and V go into the instruction's E8M0 scale operands, so they cost nothing.  P is
 //     quantised as e4m3 of 2^8 * P (the 2^8 rides in the exp2 argument and cancels against the
 //     row sum, which is summed from the unquantised values).  V is read transposed from LDS
