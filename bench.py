@@ -4,7 +4,8 @@
 One step = one attn_fwd call over the whole workload, inputs already resident in HBM.
 Default workload (the headline line): non-causal multi-head attention, bf16, B=1, N=16384,
 H=16, d=128 -- the longest point of the B*N = 16384-token sweep (the pages quote their d=128
-non-causal figure at 16k).  ``--workload`` selects the other measured configurations:
+non-causal figure at 16k); the line's config also carries every point of that sweep and the
+sweep's aggregate (total FLOPs over total time).  ``--workload`` selects the other measured configurations:
 
   sweep   bf16 non-causal d=128 H=16, N in 512..16384 with B*N = 16384 (one line per N)
   causal  bf16 causal B=2 H=16 N=8192, d in 64/128/256 (one line per d)
@@ -309,7 +310,20 @@ def main():
     with torch.cuda.stream(stream):
         if args.workload == "mha16k":
             name = "mha_n16384_b1_h16_d128"
-            out = [run_16bit(args, name, si.CONFIGS[name](), dev, stream, traffic=measured_traffic("bf16_mha16k"), cpu=True)]
+            head = run_16bit(args, name, si.CONFIGS[name](), dev, stream, traffic=measured_traffic("bf16_mha16k"),
+                             cpu=True)
+            # the rest of the B*N = 16384 sweep this figure belongs to, attached for context
+            sweep, flops, ms = {}, 0.0, 0.0
+            for n in si.CONFIGS:
+                if not n.startswith("mha_n"):
+                    continue
+                r = head if n == name else run_16bit(args, n, si.CONFIGS[n](), dev, stream)
+                sweep[f"N={r['config']['N']}"] = r["value"]
+                flops += r["config"]["flops_per_step"]
+                ms += r["ms_per_step"]
+            head["config"]["sweep_tflops"] = sweep
+            head["config"]["sweep_aggregate_tflops"] = round(flops / (ms * 1e-3) / 1e12, 2)
+            out = [head]
         elif args.workload == "sweep":
             out = [run_16bit(args, n, si.CONFIGS[n](), dev, stream)
                    for n in si.CONFIGS if n.startswith("mha_n")]
