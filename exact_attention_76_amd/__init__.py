@@ -77,10 +77,23 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream_handle(stream):
+def _stream_handle(stream, device=None):
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(device)
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _one_device(named):
+    """The device every given tensor lives on (the library launches on that device)."""
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}: all tensors must share one GPU")
+    return dev
 
 
 def _check_tensor(t, name):
@@ -156,9 +169,13 @@ def attn_fwd(q, k, v, o, lse, *, causal: bool = False, alpha: float | None = Non
     if dt == ATTN_FP16 and o.dtype != torch.float16 or dt == ATTN_BF16 and o.dtype != torch.bfloat16:
         raise TypeError("o must have the dtype of q (bf16 or fp16)")
     alpha = (1.0 / d ** 0.5) if alpha is None else float(alpha)
-    st = load_library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N,
-                                 _ptr(cu_seqlens), d, int(bool(causal)), alpha, dt,
-                                 _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), _stream_handle(stream))
+    dev = _one_device((("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("cu_seqlens", cu_seqlens),
+                       ("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)))
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, _ptr(cu_seqlens), d,
+                          int(bool(causal)), alpha, dt, _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
+                          _stream_handle(stream, dev))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd")
 
@@ -205,9 +222,13 @@ def attn_fp8_prepare(q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, *, hadamard
             raise ValueError(f"scales must be float32 {(B, H, nblk)}")
     if hadamard_signs is not None and hadamard_signs.numel() != d:
         raise ValueError("hadamard_signs must have d entries")
-    st = load_library().attn_fp8_prepare(_ptr(q), _ptr(k), _ptr(v), _ptr(q8), _ptr(k8), _ptr(v8),
-                                         _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), B, Hq, Hkv, N, d,
-                                         _ptr(hadamard_signs), _stream_handle(stream))
+    dev = _one_device((("q", q), ("k", k), ("v", v), ("q8", q8), ("k8", k8), ("v8", v8), ("q_scale", q_scale),
+                       ("k_scale", k_scale), ("v_scale", v_scale), ("hadamard_signs", hadamard_signs)))
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.attn_fp8_prepare(_ptr(q), _ptr(k), _ptr(v), _ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale),
+                                  _ptr(k_scale), _ptr(v_scale), B, Hq, Hkv, N, d, _ptr(hadamard_signs),
+                                  _stream_handle(stream, dev))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fp8_prepare")
 

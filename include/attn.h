@@ -65,7 +65,8 @@ enum {
  *   holds tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 and T = cu_seqlens[B].
  *   q, o  [T, Hq, d]        k, v [T, Hkv, d]        lse [Hq, T]
  *   N must be >= the longest sequence (it sizes the grid, so no device-to-host copy is
- *   needed); sequences longer than N are not fully processed.
+ *   needed; the library cannot check it without one).  A longer sequence is treated as its
+ *   first N tokens: its results are wrong and its rows past N are left unwritten.
  *
  * d:       64, 128 or 256 for ATTN_BF16 / ATTN_FP16; 128 for ATTN_FP8_E4M3.
  * causal:  0 = every key of the sequence is visible; 1 = key j visible to query i iff j <= i.
