@@ -253,36 +253,43 @@ def run_ceiling(args, dev, stream):
     import torch
 
     lib = ctypes.CDLL(os.path.join(ROOT, "exact_attention_76_amd", "libceiling.so"))
-    lib.ceiling_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    for fn in (lib.ceiling_mfma_bf16, lib.ceiling_mfma_fp8):
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     gen = torch.Generator(device=dev)
     gen.manual_seed(7)
-    src = torch.randn(65536 * 8, device=dev, generator=gen).to(torch.bfloat16)  # 65536 operands of 8 bf16
-    iters = 4000
+    normal = torch.randn(65536 * 8, device=dev, generator=gen)  # 1 MiB of bf16, or 512 KiB x 2 of e4m3
+    srcs = {"bf16": normal.to(torch.bfloat16),
+            "fp8": normal.to(torch.float8_e4m3fn).view(torch.uint8).repeat(2)}  # finite codes only
+    kinds = {"bf16": (lib.ceiling_mfma_bf16, 32 * 32 * 16 * 2, "v_mfma_f32_32x32x16_bf16"),
+             "fp8": (lib.ceiling_mfma_fp8, 32 * 32 * 64 * 2, "v_mfma_scale_f32_32x32x64_f8f6f4")}
     out = []
-    for waves_per_simd, grid in ((2, 512), (4, 1024)):
-        sink = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+    for dtype, (fn, flop_per_instr, instr) in kinds.items():
+        iters = 4000 if dtype == "bf16" else 2000
+        for waves_per_simd, grid in ((2, 512), (4, 1024)):
+            sink = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+            src = srcs[dtype]
 
-        def step():
-            rc = lib.ceiling_mfma_bf16(src.data_ptr(), sink.data_ptr(), iters, grid, stream.cuda_stream)
-            if rc != 0:
-                raise RuntimeError(f"ceiling_mfma_bf16 failed with hipError {rc}")
+            def step():
+                rc = fn(src.data_ptr(), sink.data_ptr(), iters, grid, stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"{instr} ceiling probe failed with hipError {rc}")
 
-        steps, warmup = max(1, min(args.steps, 10)), max(1, min(args.warmup, 5))
-        ms_wall, ms_gpu = timed(step, stream, steps, warmup)
-        flops = grid * 4 * iters * 8 * (32 * 32 * 16 * 2)
-        achieved = flops / (ms_gpu * 1e-3) / 1e12
-        out.append({
-            "metric": "sustained v_mfma_f32_32x32x16_bf16 throughput on random operands (matrix-core ceiling)",
-            "value": round(flops / (ms_wall * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps,
-            "warmup": warmup, "ms_per_step": round(ms_wall, 4), "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-            "config": {"workload": f"mfma_bf16_ceiling_{waves_per_simd}_waves_per_simd", "workgroups": grid,
-                       "waves_per_simd": waves_per_simd, "instructions_per_wave": 8 * iters,
-                       "pct_of_peak": round(100 * achieved / PEAK["bf16"], 2), "parallelism": "single GPU"},
-            "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK["bf16"], "unit": "TFLOP/s",
-                         "frac": round(achieved / PEAK["bf16"], 4), "traffic": None},
-            "cpu_baseline": None,
-        })
+            steps, warmup = max(1, min(args.steps, 10)), max(1, min(args.warmup, 5))
+            ms_wall, ms_gpu = timed(step, stream, steps, warmup)
+            flops = grid * 4 * iters * 8 * flop_per_instr
+            achieved = flops / (ms_gpu * 1e-3) / 1e12
+            out.append({
+                "metric": f"sustained {instr} throughput on random operands (matrix-core ceiling)",
+                "value": round(flops / (ms_wall * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
+                "steps": steps, "warmup": warmup, "ms_per_step": round(ms_wall, 4), "higher_is_better": True,
+                "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+                "config": {"workload": f"mfma_{dtype}_ceiling_{waves_per_simd}_waves_per_simd", "workgroups": grid,
+                           "waves_per_simd": waves_per_simd, "instructions_per_wave": 8 * iters,
+                           "pct_of_peak": round(100 * achieved / PEAK[dtype], 2), "parallelism": "single GPU"},
+                "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK[dtype], "unit": "TFLOP/s",
+                             "frac": round(achieved / PEAK[dtype], 4), "traffic": None},
+                "cpu_baseline": None,
+            })
     return out
 
 
