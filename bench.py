@@ -52,9 +52,9 @@ MEASURED_TRAFFIC = {
     "bf16_mha16k": {"kernel_source": "exact_attention_76_amd/csrc/attn_fwd.hip",
                     "sha256_prefix": "66af95da9c793b6c", "bytes": 404332430},
     "fp8_attention": {"kernel_source": "exact_attention_76_amd/csrc/fp8.hip",
-                      "sha256_prefix": "f76ba740b1f2c467", "bytes": 185607647},
+                      "sha256_prefix": "89983e69a3b13bfd", "bytes": 185535377},
     "fp8_prepare": {"kernel_source": "exact_attention_76_amd/csrc/fp8.hip",
-                    "sha256_prefix": "f76ba740b1f2c467", "bytes": 302675418},
+                    "sha256_prefix": "89983e69a3b13bfd", "bytes": 302667250},
 }
 
 

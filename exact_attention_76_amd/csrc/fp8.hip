@@ -154,8 +154,8 @@ __global__ __launch_bounds__(256) void fp8_prepare_kernel(PrepTensor t0, PrepTen
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       // |y| * 2^-e <= 448 by the choice of e, so the conversions never saturate
-      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f32_round_odd(y[4 * j] * inv), f32_round_odd(y[4 * j + 1] * inv),
-                                                     0, false);
+      const float f0 = f32_round_odd(y[4 * j] * inv);
+      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f32_round_odd(y[4 * j + 1] * inv), __float_as_int(f0), false);
       w[j] = __builtin_amdgcn_cvt_pk_fp8_f32(f32_round_odd(y[4 * j + 2] * inv), f32_round_odd(y[4 * j + 3] * inv), lo,
                                              true);
     }
@@ -363,7 +363,10 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 3 : 1)) void fwd_fp8_kern
 #pragma unroll
       for (int w = 0; w < 8; ++w) {
         const int cb = 2 * kk + (w >> 2), r0 = 4 * (w & 3);
-        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[cb][r0], s[cb][r0 + 1], 0, false);
+        // the first conversion writes the low half of the word and keeps the rest of its old
+        // input, which the second conversion overwrites: any old value will do, and the first
+        // source (dead after this instruction) costs no register initialisation
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[cb][r0], s[cb][r0 + 1], __float_as_int(s[cb][r0]), false);
         pf[w] = __builtin_amdgcn_cvt_pk_fp8_f32(s[cb][r0 + 2], s[cb][r0 + 3], lo, true);
       }
       const int sv = e8m0_of(vsc[(k0 >> 6) + kk]);
