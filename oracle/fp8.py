@@ -22,6 +22,15 @@ Readings where the pages leave a step open:
   so the block's largest magnitude lands in [224, 448] after scaling.
 * Blocks start at token 0 of every (batch, head); a short last block is scaled over its
   valid tokens only.
+* A scale must be a normal fp32 power of two, 2**-126 or more: the attention takes each scale
+  as the 8-bit exponent of the matrix instruction's scale operand (OCP E8M0), and a denormal
+  fp32 has no such exponent.  A block (or tensor) whose exponent would give a smaller scale
+  gets the smallest allowed one; its values then land among the e4m3 subnormals or round to
+  zero.  The pages never meet this case (their inputs are O(1)).
+* Per-tensor scaling, the usual practice that the digest's section 3.5 contrasts with block
+  quantisation (and the baseline of its Table 3 ablation), uses one exponent for a whole
+  tensor, chosen by the same rule from the tensor's largest magnitude; the scale arrays keep
+  their per-block shape with every entry equal.
 * The Hadamard sums are formed exactly (fp64 sums of bf16 values with +-1 weights are exact
   unless one row spans more than 2**38 in magnitude), so the code chosen for each element is
   the round-to-nearest-even of the exact rotated value.
@@ -100,40 +109,67 @@ def rotate(x: np.ndarray, signs: np.ndarray | None) -> np.ndarray:
     return (x * np.asarray(signs, dtype=np.float64)) @ hadamard(d)
 
 
-def quantize_blocks(y: np.ndarray, block: int = BLOCK):
-    """Per-(batch, head, 64-token block) power-of-two scaling and e4m3 encoding.
+# Smallest exponent of a normal fp32 (and of a usable E8M0 scale operand).
+SCALE_EXP_MIN = -126
 
-    y: [B, N, H, d] float64.  Returns (codes uint8 [B,N,H,d], exponents int [B,H,nblk]).
-    """
+
+def _nblocks(N: int, block: int) -> int:
+    return -(-N // block)
+
+
+def _encode_with(y: np.ndarray, exps: np.ndarray, block: int) -> np.ndarray:
+    """e4m3 codes of y [B, N, H, d] divided by 2**exps[b, h, token // block]."""
     B, N, H, d = y.shape
-    nblk = -(-N // block)
     codes = np.empty(y.shape, dtype=np.uint8)
-    exps = np.zeros((B, H, nblk), dtype=np.int64)
     for b in range(B):
         for h in range(H):
-            for j in range(nblk):
+            for j in range(_nblocks(N, block)):
                 t0, t1 = j * block, min(N, (j + 1) * block)
-                blk = y[b, t0:t1, h, :]
-                e = block_exponent(float(np.max(np.abs(blk))) if blk.size else 0.0)
-                exps[b, h, j] = e
-                codes[b, t0:t1, h, :] = e4m3_encode(np.ldexp(blk, -e))
-    return codes, exps
+                codes[b, t0:t1, h, :] = e4m3_encode(np.ldexp(y[b, t0:t1, h, :], -int(exps[b, h, j])))
+    return codes
 
 
-def fp8_prepare(q, k, v, signs: np.ndarray | None, block: int = BLOCK):
+def quantize_blocks(y: np.ndarray, block: int = BLOCK, e_floor: int = SCALE_EXP_MIN):
+    """Per-(batch, head, 64-token block) power-of-two scaling and e4m3 encoding.
+
+    y: [B, N, H, d] float64.  Returns (codes uint8 [B,N,H,d], exponents int [B,H,nblk]); each
+    exponent is the block's own, raised to e_floor if it is smaller.
+    """
+    B, N, H, d = y.shape
+    exps = np.zeros((B, H, _nblocks(N, block)), dtype=np.int64)
+    for b in range(B):
+        for h in range(H):
+            for j in range(exps.shape[2]):
+                blk = y[b, j * block:min(N, (j + 1) * block), h, :]
+                exps[b, h, j] = max(block_exponent(float(np.max(np.abs(blk))) if blk.size else 0.0), e_floor)
+    return _encode_with(y, exps, block), exps
+
+
+def quantize_tensor(y: np.ndarray, block: int = BLOCK, e_floor: int = SCALE_EXP_MIN):
+    """Per-tensor power-of-two scaling: one exponent, from the largest magnitude of all of y,
+    for every block.  Same outputs as :func:`quantize_blocks`."""
+    B, N, H, d = y.shape
+    e = max(block_exponent(float(np.max(np.abs(y))) if y.size else 0.0), e_floor)
+    exps = np.full((B, H, _nblocks(N, block)), e, dtype=np.int64)
+    return _encode_with(y, exps, block), exps
+
+
+def fp8_prepare(q, k, v, signs: np.ndarray | None, block: int = BLOCK, per_tensor: bool = False):
     """The full pre-pass on fp64 copies of the bf16 inputs ([B, N, H, d] each).
 
     Returns q8, k8, v8 (uint8 e4m3 codes) and q_scale, k_scale, v_scale (float32
     [B, H, nblk], powers of two).  With signs given, Q and K are rotated by D H and K's
-    scales carry the extra 1/d.
+    scales carry the extra 1/d.  per_tensor selects one scale per tensor instead of one per
+    block.  Every scale is 2**-126 or more.
     """
     d = np.shape(q)[-1]
-    q8, eq = quantize_blocks(rotate(q, signs), block)
-    k8, ek = quantize_blocks(rotate(k, signs), block)
-    v8, ev = quantize_blocks(np.asarray(v, dtype=np.float64), block)
-    ek_total = ek - (int(math.log2(d)) if signs is not None else 0)
+    shift_k = int(math.log2(d)) if signs is not None else 0
+    quant = quantize_tensor if per_tensor else quantize_blocks
+    q8, eq = quant(rotate(q, signs), block)
+    k8, ek = quant(rotate(k, signs), block, SCALE_EXP_MIN + shift_k)
+    v8, ev = quant(np.asarray(v, dtype=np.float64), block)
     to_scale = lambda e: np.ldexp(np.ones(e.shape, dtype=np.float32), e.astype(np.int32))
-    return q8, k8, v8, to_scale(eq), to_scale(ek_total), to_scale(ev)
+    return q8, k8, v8, to_scale(eq), to_scale(ek - shift_k), to_scale(ev)
 
 
 def dequantize(codes: np.ndarray, scales: np.ndarray, block: int = BLOCK) -> np.ndarray:

@@ -29,6 +29,7 @@ __all__ = [
     "varlen_inputs",
     "outlier_channels",
     "fp8_inputs",
+    "mixture_inputs",
     "hadamard_signs",
     "CONFIGS",
 ]
@@ -167,6 +168,27 @@ def fp8_inputs(B: int, N: int, H: int, d: int, *, seed: int = 5, outlier_scale: 
     inp = AttnInputs(f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v), "bf16",
                      B, N, H, H, d, False, None, seed)
     inp.meta["outlier_channels"] = chans[0] if not independent_channels else chans
+    return inp
+
+
+def mixture_inputs(B: int, N: int, H: int, d: int, *, seed: int, outlier_prob: float = 0.001,
+                   outlier_std: float = 10.0, dtype: str = "bf16") -> AttnInputs:
+    """Q, K, V whose elements are i.i.d. N(0, 1) + N(0, outlier_std**2) * Bernoulli(outlier_prob)
+    (the outlier model of the FlashAttention-3 paper's numerical-error experiment, section 4.3),
+    rounded to ``dtype``.  Per tensor, in the order Q, K, V: the N(0, 1) part, then uniforms
+    u (the element is an outlier when u < outlier_prob), then the N(0, 1) draws scaled by
+    outlier_std."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(3):
+        x = rng.standard_normal((B, N, H, d), dtype=np.float32)
+        hit = rng.random((B, N, H, d), dtype=np.float32) < np.float32(outlier_prob)
+        x += np.where(hit, rng.standard_normal((B, N, H, d), dtype=np.float32) * np.float32(outlier_std),
+                      np.float32(0.0))
+        out.append(_to_storage(x, dtype))
+    inp = AttnInputs(out[0], out[1], out[2], dtype, B, N, H, H, d, False, None, seed)
+    inp.meta["outlier_prob"] = outlier_prob
+    inp.meta["outlier_std"] = outlier_std
     return inp
 
 

@@ -5,7 +5,14 @@
   code, ties to even, and agreement with torch's CPU float8_e4m3fn cast inside the range.
 * Hadamard: H H^T = d I and equality with scipy.linalg.hadamard (Sylvester construction).
 * Incoherent processing (FlashAttention-3 digest, section 3.5): (Q D H)(K D H)^T / d = Q K^T.
-* The whole pre-pass in exact rational arithmetic (fractions.Fraction) on small inputs.
+* The whole pre-pass in exact rational arithmetic (fractions.Fraction) on small inputs, with
+  one scale per 64-token block and with one scale per tensor (the per-tensor baseline of the
+  digest's section 3.5).
+* Hand-computed codes where block and per-tensor scaling differ; the floor that keeps every
+  scale a normal fp32 power of two; a zero block does not pull a tensor's scale to 1.
+* The outlier mixture of the paper's numerical-error experiment (section 4.3): its second
+  moment and outlier count, and that the rotation lowers the error that quantising such
+  inputs costs (the direction of the paper's Table 3).
 """
 import math
 from fractions import Fraction
@@ -93,36 +100,128 @@ def _exact_code(x: Fraction) -> int:
     return best | (0x80 if x < 0 else 0)
 
 
-def test_prepare_exact_small():
-    """Rotation, block exponents and codes of the pre-pass equal exact rational arithmetic."""
+def _exact_exponent(amax: Fraction) -> int:
+    """Smallest e with amax <= 448 * 2**e, found by exact comparison (0 for amax = 0)."""
+    if not amax:
+        return 0
+    e = math.ceil(math.log2(amax / 448))
+    while amax > 448 * Fraction(2) ** e:
+        e += 1
+    while amax <= 448 * Fraction(2) ** (e - 1):
+        e -= 1
+    return e
+
+
+@pytest.mark.parametrize("per_tensor", [False, True])
+def test_prepare_exact_small(per_tensor):
+    """Rotation, exponents and codes of the pre-pass equal exact rational arithmetic."""
     inp = seeded_inputs.fp8_inputs(1, 70, 2, 16, seed=9, fraction=0.05)
     signs = seeded_inputs.hadamard_signs(16, seed=3)
     q, k, v = (bf16_to_f64(getattr(inp, n)) for n in "qkv")
-    q8, k8, v8, sq, sk, sv = fp8.fp8_prepare(q, k, v, signs)
+    q8, k8, v8, sq, sk, sv = fp8.fp8_prepare(q, k, v, signs, per_tensor=per_tensor)
     H = fp8.hadamard(16)
+    spans = ((0, 64), (64, 70))
     for name, x, codes, scales, rot in (("q", q, q8, sq, True), ("k", k, k8, sk, True),
                                         ("v", v, v8, sv, False)):
+        ex = {}  # (head, token) -> exact rotated row
         for h in range(2):
-            for blk, (t0, t1) in enumerate(((0, 64), (64, 70))):
-                ex = []
-                for t in range(t0, t1):
-                    row = [Fraction(float(z)) for z in x[0, t, h]]
-                    if rot:
-                        row = [sum(int(signs[i]) * int(H[i, j]) * row[i] for i in range(16)) for j in range(16)]
-                    ex.append(row)
-                amax = max(abs(z) for r in ex for z in r)
-                e = 0
-                if amax:
-                    e = math.ceil(math.log2(amax / 448))
-                    while amax > 448 * Fraction(2) ** e:
-                        e += 1
-                    while amax <= 448 * Fraction(2) ** (e - 1):
-                        e -= 1
+            for t in range(70):
+                row = [Fraction(float(z)) for z in x[0, t, h]]
+                if rot:
+                    row = [sum(int(signs[i]) * int(H[i, j]) * row[i] for i in range(16)) for j in range(16)]
+                ex[h, t] = row
+        e_tensor = _exact_exponent(max(abs(z) for r in ex.values() for z in r))
+        for h in range(2):
+            for blk, (t0, t1) in enumerate(spans):
+                e = e_tensor if per_tensor else _exact_exponent(
+                    max(abs(z) for t in range(t0, t1) for z in ex[h, t]))
                 want_scale = Fraction(2) ** e / (16 if name == "k" else 1)
                 assert Fraction(float(scales[0, h, blk])) == want_scale, (name, h, blk)
-                for r, t in zip(ex, range(t0, t1)):
-                    want = [_exact_code(z / Fraction(2) ** e) for z in r]
+                for t in range(t0, t1):
+                    want = [_exact_code(z / Fraction(2) ** e) for z in ex[h, t]]
                     assert codes[0, t, h].tolist() == want, (name, h, t)
+
+
+def test_block_and_tensor_scaling_by_hand():
+    """Two 64-token blocks: one holds 448, the other's largest magnitude is 1 and it holds 0.3.
+    Per block, the second block gets e = -8 (448 * 2**-9 < 1 <= 448 * 2**-8) and 0.3 * 2**8 =
+    76.8 rounds to 80 = 1.25 * 2**6, code 0 1101 010.  Per tensor, e = 0 for both blocks and
+    0.3 rounds to 0.3125 = 1.25 * 2**-2, code 0 0101 010."""
+    y = np.zeros((1, 128, 1, 4))
+    y[0, 5, 0, 2] = 448.0
+    y[0, 70, 0, 1] = -1.0
+    y[0, 100, 0, 3] = 0.3
+    codes_b, e_b = fp8.quantize_blocks(y)
+    codes_t, e_t = fp8.quantize_tensor(y)
+    assert e_b.tolist() == [[[0, -8]]] and e_t.tolist() == [[[0, 0]]]
+    assert codes_b[0, 5, 0, 2] == codes_t[0, 5, 0, 2] == 0x7E  # 448 = 1.75 * 2**8
+    assert codes_b[0, 100, 0, 3] == 0x6A and codes_t[0, 100, 0, 3] == 0x2A
+    assert codes_b[0, 70, 0, 1] == 0xF8 and codes_t[0, 70, 0, 1] == 0xB8  # -2**8 (1 1111 000), -1
+
+
+def test_tensor_scale_ignores_zero_blocks():
+    """An all-zero block has exponent 0 by itself, but the tensor's exponent comes from its
+    largest magnitude: 1e-3 gives e = -18 (448 * 2**-19 < 1e-3 <= 448 * 2**-18)."""
+    y = np.zeros((1, 192, 2, 8))
+    y[0, 150, 1, 4] = 1e-3
+    _, e_b = fp8.quantize_blocks(y)
+    _, e_t = fp8.quantize_tensor(y)
+    assert e_b[0, 1].tolist() == [0, 0, -18] and np.all(e_t == -18)
+
+
+@pytest.mark.parametrize("per_tensor", [False, True])
+def test_scale_floor(per_tensor):
+    """Magnitudes near 1e-37 would ask for scales below 2**-126; every scale is then exactly
+    2**-126 (the smallest normal fp32), K's included after its extra 1/d = 2**-4 (so K is
+    divided by 2**-122), and the codes are the
+    exact roundings of the values divided by the scale actually used."""
+    rng = np.random.default_rng(4)
+    x = np.ldexp(rng.standard_normal((1, 64, 1, 16)), -124).astype(np.float32)
+    x = bf16_to_f64(seeded_inputs.f32_to_bf16_bits(x))  # bf16 normals, amax about 2**-122
+    signs = seeded_inputs.hadamard_signs(16, seed=3)
+    q8, k8, v8, sq, sk, sv = fp8.fp8_prepare(x, x, x, signs, per_tensor=per_tensor)
+    tiny = np.float32(2.0 ** -126)
+    assert np.all(sq == tiny) and np.all(sk == tiny) and np.all(sv == tiny)
+    H = fp8.hadamard(16)
+    for t in (0, 17, 63):
+        row = [Fraction(float(z)) for z in x[0, t, 0]]
+        rot = [sum(int(signs[i]) * int(H[i, j]) * row[i] for i in range(16)) for j in range(16)]
+        assert q8[0, t, 0].tolist() == [_exact_code(z * Fraction(2) ** 126) for z in rot]
+        assert k8[0, t, 0].tolist() == [_exact_code(z * Fraction(2) ** 122) for z in rot]
+        assert v8[0, t, 0].tolist() == [_exact_code(z * Fraction(2) ** 126) for z in row]
+
+
+def test_mixture_inputs_moments():
+    """N(0,1) + N(0,100) * Bernoulli(1e-3): second moment 1 + 100 * 1e-3 = 1.1, and about
+    1e-3 * P(|N(0,100)| > 8) = 1e-3 * 0.4237 of the elements exceed 8 in magnitude (a standard
+    normal essentially never does)."""
+    inp = seeded_inputs.mixture_inputs(1, 1024, 8, 128, seed=21)
+    x = np.concatenate([seeded_inputs.bf16_bits_to_f32(getattr(inp, n)).ravel() for n in "qkv"])
+    x = x.astype(np.float64)
+    assert abs(np.mean(x * x) - 1.1) < 0.03  # standard error about 0.0033
+    n_big = int(np.sum(np.abs(x) > 8.0))
+    expect = x.size * 1e-3 * math.erfc(0.8 / math.sqrt(2.0))
+    assert abs(n_big - expect) < 6 * math.sqrt(expect), (n_big, expect)
+
+
+def test_rotation_lowers_quantisation_error_with_outliers():
+    """On the outlier mixture, attention on the dequantised inputs is closer to attention on
+    the inputs themselves when Q and K are rotated first (the paper's Table 3 finds the
+    rotation to be the main effect); with no rotation, block and per-tensor scaling give the
+    same codes up to the e4m3 subnormal range."""
+    import oracle
+
+    inp = seeded_inputs.mixture_inputs(1, 512, 2, 128, seed=8)
+    q, k, v = (bf16_to_f64(getattr(inp, n)) for n in "qkv")
+    heads, tokens = np.repeat(np.arange(2), 64), np.tile(np.arange(0, 512, 8), 2)
+    o_ref, _ = oracle.attention_rows(q, k, v, heads, tokens, causal=False, alpha=128 ** -0.5)
+    err = {}
+    for rot in (True, False):
+        prep = fp8.fp8_prepare(q, k, v, seeded_inputs.hadamard_signs(128) if rot else None)
+        qd, kd, vd = (fp8.dequantize(c, s) for c, s in zip(prep[:3], prep[3:]))
+        o, _ = oracle.attention_rows(qd, kd, vd, heads, tokens, causal=False, alpha=128 ** -0.5)
+        err[rot] = float(np.sqrt(np.mean((o - o_ref) ** 2)))
+    assert err[True] * 1.2 < err[False], err
 
 
 def test_dequantized_error_bound():
