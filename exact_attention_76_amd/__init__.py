@@ -9,6 +9,7 @@ Entry points carry the names of the C ABI:
 * :func:`attn_fwd` -- O and LSE of exact attention (bf16 / fp16 / fp8-e4m3 inputs; dense or
   packed variable-length; causal or not; grouped-query heads).
 * :func:`attn_fp8_prepare` -- Hadamard rotation + per-block power-of-two e4m3 quantisation.
+* :func:`attn_fp8_prepare_scaling` -- the same with a choice of per-block or per-tensor scales.
 * :func:`attn_strerror` -- text of a status code.
 
 Helpers :func:`attention` and :func:`fp8_prepare` allocate the outputs and call the above.
@@ -21,8 +22,9 @@ import re
 
 import torch
 
-__all__ = ["AttnError", "attn_fwd", "attn_fp8_prepare", "attn_strerror", "attention", "fp8_prepare",
-           "load_library", "LIB_PATH", "ATTN_BF16", "ATTN_FP16", "ATTN_FP8_E4M3"]
+__all__ = ["AttnError", "attn_fwd", "attn_fp8_prepare", "attn_fp8_prepare_scaling", "attn_strerror", "attention",
+           "fp8_prepare", "load_library", "LIB_PATH", "ATTN_BF16", "ATTN_FP16", "ATTN_FP8_E4M3",
+           "ATTN_FP8_SCALE_BLOCK", "ATTN_FP8_SCALE_TENSOR"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libattn.so")
@@ -30,6 +32,7 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "attn.h")
 
 ATTN_BF16, ATTN_FP16, ATTN_FP8_E4M3 = 0, 1, 2
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_ALIGN, ATTN_ERR_HIP = 0, -1, -2, -3, -4
+ATTN_FP8_SCALE_BLOCK, ATTN_FP8_SCALE_TENSOR = 0, 1
 
 _lib = None
 
@@ -57,6 +60,8 @@ def load_library(build_if_missing: bool = True):
     lib.attn_fwd.restype = I
     lib.attn_fp8_prepare.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, P]
     lib.attn_fp8_prepare.restype = I
+    lib.attn_fp8_prepare_scaling.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, I, P]
+    lib.attn_fp8_prepare_scaling.restype = I
     lib.attn_strerror.argtypes = [I]
     lib.attn_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -196,19 +201,17 @@ def attention(q, k, v, *, causal: bool = False, alpha: float | None = None, cu_s
     return o, lse
 
 
-def attn_fp8_prepare(q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, *, hadamard_signs=None,
-                     stream=None) -> None:
-    """Enqueue the FP8 pre-pass: bf16 q/k/v [B, N, H, d] -> e4m3 codes + fp32 block scales
-    [B, H, ceil(N/64)].  ``hadamard_signs``: int8 [d] of +-1 on the GPU, or None for no rotation."""
-    for name, t in (("q", q), ("k", k), ("v", v), ("q8", q8), ("k8", k8), ("v8", v8),
-                    ("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
-        _check_tensor(t, name)
+def _prepare_call(q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, hadamard_signs, name):
+    """Check the pre-pass tensors; return the device and the C arguments before the mode."""
+    for nm, t in (("q", q), ("k", k), ("v", v), ("q8", q8), ("k8", k8), ("v8", v8),
+                  ("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
+        _check_tensor(t, nm)
     if hadamard_signs is not None:
         _check_tensor(hadamard_signs, "hadamard_signs")
         if hadamard_signs.dtype != torch.int8:
             raise TypeError("hadamard_signs must be int8")
     if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
-        raise TypeError("attn_fp8_prepare takes bf16 inputs")
+        raise TypeError(f"{name} takes bf16 inputs")
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
     nblk = -(-N // 64)
@@ -224,17 +227,39 @@ def attn_fp8_prepare(q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, *, hadamard
         raise ValueError("hadamard_signs must have d entries")
     dev = _one_device((("q", q), ("k", k), ("v", v), ("q8", q8), ("k8", k8), ("v8", v8), ("q_scale", q_scale),
                        ("k_scale", k_scale), ("v_scale", v_scale), ("hadamard_signs", hadamard_signs)))
+    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
+            B, Hq, Hkv, N, d, _ptr(hadamard_signs))
+    return dev, args
+
+
+def attn_fp8_prepare(q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, *, hadamard_signs=None,
+                     stream=None) -> None:
+    """Enqueue the FP8 pre-pass: bf16 q/k/v [B, N, H, d] -> e4m3 codes + fp32 block scales
+    [B, H, ceil(N/64)].  ``hadamard_signs``: int8 [d] of +-1 on the GPU, or None for no rotation."""
+    dev, args = _prepare_call(q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, hadamard_signs, "attn_fp8_prepare")
     lib = load_library()
     with torch.cuda.device(dev):
-        st = lib.attn_fp8_prepare(_ptr(q), _ptr(k), _ptr(v), _ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale),
-                                  _ptr(k_scale), _ptr(v_scale), B, Hq, Hkv, N, d, _ptr(hadamard_signs),
-                                  _stream_handle(stream, dev))
+        st = lib.attn_fp8_prepare(*args, _stream_handle(stream, dev))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fp8_prepare")
 
 
-def fp8_prepare(q, k, v, *, hadamard_signs=None, stream=None):
-    """Allocate the e4m3 tensors (as uint8 codes) and scales and call :func:`attn_fp8_prepare`."""
+def attn_fp8_prepare_scaling(q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, *, scaling: int,
+                             hadamard_signs=None, stream=None) -> None:
+    """:func:`attn_fp8_prepare` with ``scaling`` = ATTN_FP8_SCALE_BLOCK (one scale per 64-token
+    block) or ATTN_FP8_SCALE_TENSOR (one scale per tensor, repeated in every block entry)."""
+    dev, args = _prepare_call(q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, hadamard_signs,
+                              "attn_fp8_prepare_scaling")
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.attn_fp8_prepare_scaling(*args, int(scaling), _stream_handle(stream, dev))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fp8_prepare_scaling")
+
+
+def fp8_prepare(q, k, v, *, hadamard_signs=None, per_tensor: bool = False, stream=None):
+    """Allocate the e4m3 tensors (as uint8 codes) and scales and run the pre-pass, with one scale
+    per 64-token block (:func:`attn_fp8_prepare`) or, with ``per_tensor``, one per tensor."""
     B, N, Hq, d = q.shape
     Hkv = k.shape[2]
     nblk = -(-N // 64)
@@ -245,5 +270,9 @@ def fp8_prepare(q, k, v, *, hadamard_signs=None, stream=None):
     qs = torch.empty((B, Hq, nblk), dtype=torch.float32, device=dev)
     ks = torch.empty((B, Hkv, nblk), dtype=torch.float32, device=dev)
     vs = torch.empty((B, Hkv, nblk), dtype=torch.float32, device=dev)
-    attn_fp8_prepare(q, k, v, q8, k8, v8, qs, ks, vs, hadamard_signs=hadamard_signs, stream=stream)
+    if per_tensor:
+        attn_fp8_prepare_scaling(q, k, v, q8, k8, v8, qs, ks, vs, scaling=ATTN_FP8_SCALE_TENSOR,
+                                 hadamard_signs=hadamard_signs, stream=stream)
+    else:
+        attn_fp8_prepare(q, k, v, q8, k8, v8, qs, ks, vs, hadamard_signs=hadamard_signs, stream=stream)
     return q8, k8, v8, qs, ks, vs

@@ -13,6 +13,11 @@
 //     registers, two across the lane quad), so the rotated values are exact; the block's
 //     largest magnitude picks the exponent and every element is rounded to e4m3 from its exact
 //     fp64 value (fp64 -> fp32 rounded to odd, then the hardware's nearest-even conversion).
+//     Per-tensor scaling (the usual practice that block quantisation replaces) takes three
+//     launches: the same kernel writes each block's exponent into its scale slot, one
+//     workgroup per tensor reduces the slots to the tensor's exponent and writes its scale
+//     everywhere, and the kernel runs again with that exponent.  Every scale is kept at
+//     2^-126 or more, a normal fp32 whose exponent is the E8M0 operand the attention uses.
 //   * Attention: the plain loop of the 16-bit kernel (scores formed transposed, online softmax
 //     in fp32, K/V tiles copied buffer-to-LDS, two LDS stages, one barrier per tile) with four
 //     waves (128 queries) per workgroup and three workgroups per CU -- the softmax is the larger
@@ -23,6 +28,7 @@
 //     row sum, which is summed from the unquantised values).  V is read transposed from LDS
 //     with ds_read_b64_tr_b8, the key order matching the byte order of the P operand.
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -76,6 +82,18 @@ __device__ __forceinline__ double shfl_xor_d(double x, int mask) {
   return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
 
+// Smallest exponent of a normal fp32 scale.
+constexpr int kScaleExpMin = -126;
+
+// What one launch of the pre-pass kernel does.
+enum PrepPass : int {
+  kPrepBlock = 0,        // per-block scaling: codes and block scales
+  kPrepTensorScan = 1,   // per-tensor, first pass: each block's own exponent, as an int, into its
+                         // scale slot (INT_MIN for an all-zero block); no codes
+  kPrepTensorCodes = 2,  // per-tensor, last pass: codes with the exponent the slot now holds
+};
+
+template <int PASS>
 __global__ __launch_bounds__(256) void fp8_prepare_kernel(PrepTensor t0, PrepTensor t1, PrepTensor t2, int B, int N,
                                                           int nblk, const signed char* __restrict__ signs) {
   const PrepTensor t = blockIdx.y == 0 ? t0 : (blockIdx.y == 1 ? t1 : t2);
@@ -128,42 +146,81 @@ __global__ __launch_bounds__(256) void fp8_prepare_kernel(PrepTensor t0, PrepTen
       }
     }
   }
-  // block amax (exact, fp64)
-  double amax = 0.0;
-  if (valid) {
+  float* const slot = t.scale + ((int64_t)b * H + h) * nblk + blk;
+  int e;
+  if constexpr (PASS == kPrepTensorCodes) {
+    e = (int)((__float_as_uint(*slot) >> 23) & 0xFF) - 127 + t.scale_shift;  // slot holds 2^(e - shift)
+  } else {
+    // block amax (exact, fp64)
+    double amax = 0.0;
+    if (valid) {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(y[i]));
-  }
+      for (int i = 0; i < 32; ++i) amax = fmax(amax, fabs(y[i]));
+    }
 #pragma unroll
-  for (int m = 1; m < 64; m <<= 1) amax = fmax(amax, shfl_xor_d(amax, m));
-  __shared__ double wmax[4];
-  if ((tid & 63) == 0) wmax[tid >> 6] = amax;
-  __syncthreads();
-  amax = fmax(fmax(wmax[0], wmax[1]), fmax(wmax[2], wmax[3]));
-  // smallest e with amax <= 448 * 2^e: amax = f * 2^ex, f in [0.5, 1); 448 = 0.875 * 2^9
-  int e = 0;
-  if (amax > 0.0) {
-    const long long bits = __double_as_longlong(amax);
-    const int ex = (int)((bits >> 52) & 0x7FF) - 1022;
-    const long long frac = bits & 0xFFFFFFFFFFFFFLL;  // f = (1 + frac / 2^52) / 2
-    e = (frac <= (3LL << 50)) ? ex - 9 : ex - 8;
+    for (int m = 1; m < 64; m <<= 1) amax = fmax(amax, shfl_xor_d(amax, m));
+    __shared__ double wmax[4];
+    if ((tid & 63) == 0) wmax[tid >> 6] = amax;
+    __syncthreads();
+    amax = fmax(fmax(wmax[0], wmax[1]), fmax(wmax[2], wmax[3]));
+    // smallest e with amax <= 448 * 2^e: amax = f * 2^ex, f in [0.5, 1); 448 = 0.875 * 2^9
+    e = 0;
+    if (amax > 0.0) {
+      const long long bits = __double_as_longlong(amax);
+      const int ex = (int)((bits >> 52) & 0x7FF) - 1022;
+      const long long frac = bits & 0xFFFFFFFFFFFFFLL;  // f = (1 + frac / 2^52) / 2
+      e = (frac <= (3LL << 50)) ? ex - 9 : ex - 8;
+    }
+    if constexpr (PASS == kPrepTensorScan) {
+      if (tid == 0) *slot = __int_as_float(amax > 0.0 ? e : INT_MIN);
+      return;
+    }
+    e = max(e, t.scale_shift + kScaleExpMin);  // the scale 2^(e - shift) stays a normal fp32
   }
   const double inv = __longlong_as_double((long long)(1023 - e) << 52);  // 2^-e, exact
   if (valid) {
     uint32_t w[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      // |y| * 2^-e <= 448 by the choice of e, so the conversions never saturate
-      const float f0 = f32_round_odd(y[4 * j] * inv);
-      const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f0, f32_round_odd(y[4 * j + 1] * inv), __float_as_int(f0), false);
-      w[j] = __builtin_amdgcn_cvt_pk_fp8_f32(f32_round_odd(y[4 * j + 2] * inv), f32_round_odd(y[4 * j + 3] * inv), lo,
-                                             true);
+      // |y| * 2^-e <= 448 by the choice of e, so the conversions never saturate.  The + 0.0f
+      // turns an exact -0 into +0 (an exact zero encodes as +0) and leaves every nonzero value,
+      // fp32 subnormals included (denormals are kept), as it is.
+      const float f0 = f32_round_odd(y[4 * j] * inv) + 0.0f;
+      const int lo =
+          __builtin_amdgcn_cvt_pk_fp8_f32(f0, f32_round_odd(y[4 * j + 1] * inv) + 0.0f, __float_as_int(f0), false);
+      w[j] = __builtin_amdgcn_cvt_pk_fp8_f32(f32_round_odd(y[4 * j + 2] * inv) + 0.0f,
+                                             f32_round_odd(y[4 * j + 3] * inv) + 0.0f, lo, true);
     }
     u32x4* dst = reinterpret_cast<u32x4*>(t.x8 + rowoff * 128 + 32 * p);
     dst[0] = u32x4{w[0], w[1], w[2], w[3]};
     dst[1] = u32x4{w[4], w[5], w[6], w[7]};
   }
-  if (tid == 0) t.scale[((int64_t)b * H + h) * nblk + blk] = __uint_as_float((uint32_t)(e - t.scale_shift + 127) << 23);
+  if constexpr (PASS == kPrepBlock) {
+    if (tid == 0) *slot = __uint_as_float((uint32_t)(e - t.scale_shift + 127) << 23);
+  }
+}
+
+// Per-tensor scaling, middle pass: one workgroup per tensor takes the largest block exponent
+// left in its scale slots by the scan pass (an all-zero tensor gets 0), raises it to the
+// floor, and writes the tensor's scale into every slot.  Every slot is read before the
+// barrier inside the reduction and written after it.
+__global__ __launch_bounds__(1024) void fp8_tensor_scale_kernel(PrepTensor t0, PrepTensor t1, PrepTensor t2, int B,
+                                                                int nblk) {
+  const PrepTensor t = blockIdx.x == 0 ? t0 : (blockIdx.x == 1 ? t1 : t2);
+  const int64_t n = (int64_t)B * t.H * nblk;
+  int m = INT_MIN;
+  for (int64_t i = threadIdx.x; i < n; i += 1024) m = max(m, __float_as_int(t.scale[i]));
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) m = max(m, __shfl_xor(m, s));
+  __shared__ int wmax[16];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = wmax[0];
+#pragma unroll
+  for (int w = 1; w < 16; ++w) m = max(m, wmax[w]);
+  const int e = max(m == INT_MIN ? 0 : m, t.scale_shift + kScaleExpMin);
+  const float scale = __uint_as_float((uint32_t)(e - t.scale_shift + 127) << 23);
+  for (int64_t i = threadIdx.x; i < n; i += 1024) t.scale[i] = scale;
 }
 
 // ============================================================================================
@@ -433,8 +490,20 @@ hipError_t launch_fp8_prepare(const PrepareArgs& a, hipStream_t stream) {
   PrepTensor tv{static_cast<const uint16_t*>(a.v), static_cast<uint8_t*>(a.v8), a.v_scale, a.Hkv, 0, 0};
   const long long grid = (long long)a.B * a.Hq * nblk;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(fp8_prepare_kernel, dim3((unsigned)grid, 3), dim3(256), 0, stream, tq, tk, tv, a.B, a.N, nblk,
-                     a.signs);
+  if (!a.per_tensor) {
+    hipLaunchKernelGGL(fp8_prepare_kernel<kPrepBlock>, dim3((unsigned)grid, 3), dim3(256), 0, stream, tq, tk, tv, a.B,
+                       a.N, nblk, a.signs);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(fp8_prepare_kernel<kPrepTensorScan>, dim3((unsigned)grid, 3), dim3(256), 0, stream, tq, tk, tv,
+                     a.B, a.N, nblk, a.signs);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(fp8_tensor_scale_kernel, dim3(3), dim3(1024), 0, stream, tq, tk, tv, a.B, nblk);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(fp8_prepare_kernel<kPrepTensorCodes>, dim3((unsigned)grid, 3), dim3(256), 0, stream, tq, tk, tv,
+                     a.B, a.N, nblk, a.signs);
   return hipGetLastError();
 }
 

@@ -41,6 +41,7 @@ struct PrepareArgs {
   float* v_scale;
   int B, Hq, Hkv, N, d;
   const signed char* signs;
+  int per_tensor;             // one scale per tensor instead of one per 64-token block
 };
 
 hipError_t launch_fp8_prepare(const PrepareArgs& a, hipStream_t stream);

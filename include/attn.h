@@ -75,8 +75,9 @@ enum {
  * q_scale, k_scale, v_scale (ATTN_FP8_E4M3 only, else ignored): fp32 device arrays of
  *   powers of two, [B, Hq, ceil(N/64)] for q and [B, Hkv, ceil(N/64)] for k and v; block c
  *   covers tokens 64c .. 64c+63 of a (batch, head).  The attention inputs are
- *   e4m3(x) * scale (digest section 3.5, block quantisation).  FP8 currently requires the
- *   dense layout and causal == 0.
+ *   e4m3(x) * scale (digest section 3.5, block quantisation).  Each scale must be a normal
+ *   fp32 power of two, 2^-126 .. 2^127: the kernel passes its exponent to the matrix
+ *   instruction as an E8M0 scale.  FP8 currently requires the dense layout and causal == 0.
  * lse:     fp32, natural log, in units of the scaled scores S.  A row without visible keys
  *          gets O = 0 and L = -inf.
  *
@@ -105,8 +106,12 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * every element is divided by 2^e and rounded to the nearest e4m3 value (ties to even,
  * sign kept), and the block scale 2^e is written -- times 1/d for k when rotated, so that
  * (q8 * q_scale) . (k8 * k_scale) approximates q . k.
+ * If that scale would be below 2^-126 (amax under 448 * 2^-127, about 2.6e-36, or under
+ * 448 * 2^-120 for rotated k), e is raised until the scale is 2^-126, so every scale is a
+ * normal fp32 as attn_fwd requires.
  * Outputs q8/k8/v8: uint8 e4m3 codes in the input layouts; scales fp32 [B, H, ceil(N/64)].
  * The rotated sums are formed in fp64, so each code is the rounding of the exact value.
+ * Inputs must be finite.
  */
 int attn_fp8_prepare(const void* q, const void* k, const void* v,
                      void* q8, void* k8, void* v8,
@@ -114,6 +119,32 @@ int attn_fp8_prepare(const void* q, const void* k, const void* v,
                      int B, int Hq, int Hkv, int N, int d,
                      const signed char* hadamard_signs,
                      hipStream_t stream);
+
+/* Granularity of the FP8 pre-pass's power-of-two scales. */
+typedef enum {
+  ATTN_FP8_SCALE_BLOCK = 0,  /* one scale per (batch, head, block of 64 tokens) */
+  ATTN_FP8_SCALE_TENSOR = 1  /* one scale per tensor */
+} attn_fp8_scaling_t;
+
+/*
+ * attn_fp8_prepare_scaling -- attn_fp8_prepare with a choice of scale granularity.
+ *
+ * ATTN_FP8_SCALE_BLOCK is exactly attn_fp8_prepare.  ATTN_FP8_SCALE_TENSOR is per-tensor
+ * scaling, the usual practice that the digest's section 3.5 contrasts with block quantisation
+ * and the baseline of the FlashAttention-3 paper's FP8 error ablation (section 4.3, Table 3):
+ * e is chosen by the same rule from the largest magnitude of the whole (rotated) tensor, all
+ * batches and heads, and that one scale is written into every [b, h, block] entry, so the
+ * outputs feed attn_fwd unchanged.  The per-tensor pre-pass takes three kernel launches on
+ * `stream` and uses the scale arrays as working storage between them: their contents are
+ * defined only once all three have run.  Any other value of `scaling` returns
+ * ATTN_ERR_INVALID.  Arguments, layouts and errors are otherwise those of attn_fp8_prepare.
+ */
+int attn_fp8_prepare_scaling(const void* q, const void* k, const void* v,
+                             void* q8, void* k8, void* v8,
+                             float* q_scale, float* k_scale, float* v_scale,
+                             int B, int Hq, int Hkv, int N, int d,
+                             const signed char* hadamard_signs, attn_fp8_scaling_t scaling,
+                             hipStream_t stream);
 
 /* Static description of a status code. */
 const char* attn_strerror(int status);

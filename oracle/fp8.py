@@ -27,6 +27,9 @@ Readings where the pages leave a step open:
   fp32 has no such exponent.  A block (or tensor) whose exponent would give a smaller scale
   gets the smallest allowed one; its values then land among the e4m3 subnormals or round to
   zero.  The pages never meet this case (their inputs are O(1)).
+* The code of an element follows its exact value: an exact zero (also a -0.0 input, or a
+  rotated sum that cancels exactly) encodes as +0, and a nonzero value too small for e4m3
+  rounds to the zero of its own sign.
 * Per-tensor scaling, the usual practice that the digest's section 3.5 contrasts with block
   quantisation (and the baseline of its Table 3 ablation), uses one exponent for a whole
   tensor, chosen by the same rule from the tensor's largest magnitude; the scale arrays keep
@@ -125,7 +128,9 @@ def _encode_with(y: np.ndarray, exps: np.ndarray, block: int) -> np.ndarray:
         for h in range(H):
             for j in range(_nblocks(N, block)):
                 t0, t1 = j * block, min(N, (j + 1) * block)
-                codes[b, t0:t1, h, :] = e4m3_encode(np.ldexp(y[b, t0:t1, h, :], -int(exps[b, h, j])))
+                # + 0.0 clears the sign of an exact zero (a -0.0 input, or a rotated sum that
+                # is exactly zero), so the code follows the value: exact zero -> +0.
+                codes[b, t0:t1, h, :] = e4m3_encode(np.ldexp(y[b, t0:t1, h, :], -int(exps[b, h, j])) + 0.0)
     return codes
 
 

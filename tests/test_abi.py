@@ -19,7 +19,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = ea.header_functions()
-    assert set(names) == {"attn_fwd", "attn_fp8_prepare", "attn_strerror"}
+    assert set(names) == {"attn_fwd", "attn_fp8_prepare", "attn_fp8_prepare_scaling", "attn_strerror"}
     out = subprocess.run(["nm", "-D", "--defined-only", ea.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
@@ -96,3 +96,24 @@ def prep(lib, q=A, k=A, v=A, q8=A, k8=A, v8=A, qs=A, ks=A, vs=A, B=1, Hq=2, Hkv=
 ])
 def test_prepare_validation(lib, kw, status):
     assert prep(lib, **kw) == status
+
+
+def prep_scaling(lib, scaling, q=A, k=A, v=A, q8=A, k8=A, v8=A, qs=A, ks=A, vs=A, B=1, Hq=2, Hkv=2, N=128,
+                 d=128):
+    P = ctypes.c_void_p
+    return lib.attn_fp8_prepare_scaling(P(q), P(k), P(v), P(q8), P(k8), P(v8), P(qs), P(ks), P(vs),
+                                        B, Hq, Hkv, N, d, None, scaling, None)
+
+
+@pytest.mark.parametrize("scaling,kw,status", [
+    (2, {}, ea.ATTN_ERR_INVALID),
+    (-1, {}, ea.ATTN_ERR_INVALID),
+    (ea.ATTN_FP8_SCALE_TENSOR, dict(q=0), ea.ATTN_ERR_INVALID),
+    (ea.ATTN_FP8_SCALE_TENSOR, dict(vs=0), ea.ATTN_ERR_INVALID),
+    (ea.ATTN_FP8_SCALE_TENSOR, dict(Hq=3, Hkv=2), ea.ATTN_ERR_INVALID),
+    (ea.ATTN_FP8_SCALE_TENSOR, dict(d=256), ea.ATTN_ERR_UNSUPPORTED),
+    (ea.ATTN_FP8_SCALE_TENSOR, dict(v8=A + 3), ea.ATTN_ERR_ALIGN),
+    (ea.ATTN_FP8_SCALE_BLOCK, dict(B=0), ea.ATTN_ERR_INVALID),
+])
+def test_prepare_scaling_validation(lib, scaling, kw, status):
+    assert prep_scaling(lib, scaling, **kw) == status

@@ -2,7 +2,9 @@
 
 * attn_fp8_prepare against the oracle's emulation (oracle/fp8.py): e4m3 codes and block scales
   must match bit for bit (integer work decided from exact fp64 values on both sides), with and
-  without the Hadamard rotation, for ragged token counts, grouped heads and the full workload.
+  without the Hadamard rotation, for ragged token counts, grouped heads and the full workload;
+  the same for attn_fp8_prepare_scaling's per-tensor scales, and for blocks so small that their
+  scales sit on the 2^-126 floor, or all zero.
 * attn_fwd on e4m3 inputs against the fp64 oracle run on the *unquantised* bf16 inputs (the
   error measure of the FlashAttention-3 digest's section 3.5 / Table 3): O RMSE <= 3e-2, or the
   floor that quantising the inputs sets for any implementation (exact attention on the
@@ -25,19 +27,19 @@ def _dev_bf16(bits):
     return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def gpu_prepare(inp, signs):
+def gpu_prepare(inp, signs, per_tensor=False):
     import exact_attention_76_amd as ea
 
     q, k, v = (_dev_bf16(getattr(inp, n)) for n in "qkv")
     sg = None if signs is None else torch.from_numpy(signs).cuda()
-    out = ea.fp8_prepare(q, k, v, hadamard_signs=sg)
+    out = ea.fp8_prepare(q, k, v, hadamard_signs=sg, per_tensor=per_tensor)
     torch.cuda.synchronize()
     return out
 
 
-def oracle_prepare(inp, signs):
+def oracle_prepare(inp, signs, per_tensor=False):
     q, k, v = (oracle.bf16_to_f64(getattr(inp, n)) for n in "qkv")
-    return ofp8.fp8_prepare(q, k, v, signs)
+    return ofp8.fp8_prepare(q, k, v, signs, per_tensor=per_tensor)
 
 
 def _assert_prepare_equal(got, want, what):
@@ -66,6 +68,49 @@ def test_prepare_bit_exact_full_workload():
     signs = si.hadamard_signs(128, seed=55)
     gu.say("fp8 prepare full workload")
     _assert_prepare_equal(gpu_prepare(inp, signs), oracle_prepare(inp, signs), "prepare full")
+
+
+@pytest.mark.parametrize("rotate", [True, False])
+def test_prepare_per_tensor_bit_exact_ragged_gqa(rotate):
+    """One scale per tensor: the largest magnitude sits in one head of one batch, and the
+    tensors' exponents differ (Q widened, V narrowed)."""
+    inp = si.dense_inputs(3, 130, 4, 128, Hkv=2, seed=602)
+    inp.q = si.f32_to_bf16_bits(si.bf16_bits_to_f32(inp.q) * np.float32(37.0))
+    inp.v = si.f32_to_bf16_bits(si.bf16_bits_to_f32(inp.v) * np.float32(2.0 ** -20))
+    signs = si.hadamard_signs(128, seed=55) if rotate else None
+    gu.say("fp8 prepare per tensor ragged/GQA", rotate)
+    got, want = gpu_prepare(inp, signs, True), oracle_prepare(inp, signs, True)
+    assert len(np.unique(want[3])) == 1 and want[3].flat[0] != want[5].flat[0]
+    _assert_prepare_equal(got, want, f"per-tensor prepare rotate={rotate}")
+
+
+def test_prepare_per_tensor_bit_exact_full_workload():
+    inp = si.CONFIGS["fp8_b2_h16_n8192_d128"]()
+    signs = si.hadamard_signs(128, seed=55)
+    gu.say("fp8 prepare per tensor full workload")
+    _assert_prepare_equal(gpu_prepare(inp, signs, True), oracle_prepare(inp, signs, True), "per-tensor full")
+
+
+@pytest.mark.parametrize("per_tensor", [False, True])
+@pytest.mark.parametrize("rotate", [True, False])
+def test_prepare_scale_floor_and_zero_blocks(per_tensor, rotate):
+    """Q holds magnitudes near 2^-124 (some bf16 subnormal): their scales would fall below
+    2^-126 and sit on that floor.  K's first block and V's middle block are all zero; per
+    tensor, K's scale still comes from its nonzero blocks, while V stays at ordinary size."""
+    inp = si.dense_inputs(1, 200, 2, 128, seed=603)
+    inp.q = si.f32_to_bf16_bits(si.bf16_bits_to_f32(inp.q) * np.float32(2.0 ** -124))
+    k = si.bf16_bits_to_f32(inp.k) * np.float32(2.0 ** -100)
+    k[:, :64] = 0.0
+    inp.k = si.f32_to_bf16_bits(k)
+    v = si.bf16_bits_to_f32(inp.v)
+    v[:, 64:128] = 0.0
+    inp.v = si.f32_to_bf16_bits(v)
+    signs = si.hadamard_signs(128, seed=55) if rotate else None
+    gu.say("fp8 prepare floor/zero blocks", per_tensor, rotate)
+    want = oracle_prepare(inp, signs, per_tensor)
+    assert np.all(want[3] == np.float32(2.0 ** -126))  # the floor is exercised
+    _assert_prepare_equal(gpu_prepare(inp, signs, per_tensor), want,
+                          f"floor/zero prepare per_tensor={per_tensor} rotate={rotate}")
 
 
 def gpu_fp8_attention(inp, signs):

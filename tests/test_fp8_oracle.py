@@ -159,6 +159,22 @@ def test_block_and_tensor_scaling_by_hand():
     assert codes_b[0, 70, 0, 1] == 0xF8 and codes_t[0, 70, 0, 1] == 0xB8  # -2**8 (1 1111 000), -1
 
 
+def test_exact_zero_encodes_as_plus_zero():
+    """-0.0 inputs and rotated sums that are exactly zero give the code of +0; a nonzero value
+    below half the smallest subnormal gives the zero of its own sign."""
+    y = np.zeros((1, 2, 1, 8))
+    y[0, 0, 0, :4] = -0.0
+    y[0, 0, 0, 4] = 1.0  # block exponent -8
+    y[0, 1, 0, 5] = -2.0 ** -20  # 2**-12 after scaling by 2**8: below 2**-10, rounds to -0
+    codes, e = fp8.quantize_blocks(y)
+    assert e.tolist() == [[[-8]]]
+    assert codes[0, 0, 0, :4].tolist() == [0, 0, 0, 0] and codes[0, 1, 0, 5] == 0x80
+    signs = np.array([-1, 1, -1, -1, 1, 1, -1, 1], dtype=np.int8)
+    x = np.full((1, 3, 1, 8), -0.0)
+    q8, k8, _, _, _, _ = fp8.fp8_prepare(x, x, x, signs)
+    assert np.all(q8 == 0) and np.all(k8 == 0)
+
+
 def test_tensor_scale_ignores_zero_blocks():
     """An all-zero block has exponent 0 by itself, but the tensor's exponent comes from its
     largest magnitude: 1e-3 gives e = -18 (448 * 2**-19 < 1e-3 <= 448 * 2**-18)."""
