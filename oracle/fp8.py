@@ -177,6 +177,58 @@ def fp8_prepare(q, k, v, signs: np.ndarray | None, block: int = BLOCK, per_tenso
     return q8, k8, v8, to_scale(eq), to_scale(ek - shift_k), to_scale(ev)
 
 
+def fp8_prepare_varlen(q, k, v, cu_seqlens, max_seqlen: int, signs: np.ndarray | None, block: int = BLOCK,
+                       per_tensor: bool = False):
+    """The pre-pass on packed sequences: q [T, Hq, d], k and v [T, Hkv, d] (fp64 copies of the
+    bf16 inputs); sequence b holds tokens cu_seqlens[b] .. cu_seqlens[b+1]-1.
+
+    Blocks start at every sequence's first token, so each sequence is quantised as the dense
+    pre-pass would quantise it alone.  Scales are float32 [nseq, H, ceil(max_seqlen/64)].  With
+    per-block scales, entries past a sequence's last block are NaN (not defined); with
+    per_tensor, one exponent comes from the largest magnitude of the whole packed tensor and
+    every entry holds its scale.
+    """
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    nseq = len(cu) - 1
+    d = np.shape(q)[-1]
+    shift_k = int(math.log2(d)) if signs is not None else 0
+    nblk = _nblocks(max_seqlen, block)
+    out_codes, out_scales = [], []
+    for x, rot, floor, shift in ((q, True, SCALE_EXP_MIN, 0), (k, True, SCALE_EXP_MIN + shift_k, shift_k),
+                                 (v, False, SCALE_EXP_MIN, 0)):
+        y = rotate(x, signs) if rot else np.asarray(x, dtype=np.float64)
+        T, H, _ = y.shape
+        codes = np.empty(y.shape, dtype=np.uint8)
+        exps = np.full((nseq, H, nblk), np.nan)
+        e_tensor = max(block_exponent(float(np.max(np.abs(y))) if y.size else 0.0), floor)
+        for b in range(nseq):
+            seq = y[None, cu[b]:cu[b + 1]]  # [1, n_b, H, d]
+            if per_tensor:
+                e = np.full((1, H, _nblocks(seq.shape[1], block)), e_tensor, dtype=np.int64)
+                c = _encode_with(seq, e, block)
+                exps[b] = e_tensor
+            else:
+                c, e = quantize_blocks(seq, block, floor)
+                exps[b, :, :e.shape[2]] = e[0]
+            codes[cu[b]:cu[b + 1]] = c[0]
+        out_codes.append(codes)
+        out_scales.append(np.where(np.isnan(exps), np.float32(np.nan),
+                                   np.ldexp(np.float32(1.0), np.nan_to_num(exps - shift).astype(np.int32))
+                                   ).astype(np.float32))
+    return (*out_codes, *out_scales)
+
+
+def dequantize_varlen(codes: np.ndarray, scales: np.ndarray, cu_seqlens, block: int = BLOCK) -> np.ndarray:
+    """codes [T,H,d] of packed sequences with scales [nseq,H,nblk] -> float64 [T,H,d] (exact)."""
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    out = np.empty(codes.shape, dtype=np.float64)
+    for b in range(len(cu) - 1):
+        seq = codes[None, cu[b]:cu[b + 1]]
+        nb = _nblocks(seq.shape[1], block)
+        out[cu[b]:cu[b + 1]] = dequantize(seq, scales[b:b + 1, :, :nb], block)[0]
+    return out
+
+
 def dequantize(codes: np.ndarray, scales: np.ndarray, block: int = BLOCK) -> np.ndarray:
     """codes [B,N,H,d] with scales [B,H,nblk] -> float64 [B,N,H,d] (exact)."""
     B, N, H, d = codes.shape

@@ -1,10 +1,11 @@
 """Planted mistakes in copies of the FP8 pre-pass oracle (oracle/fp8.py) must each fail a pin.
 
 Each mutation is a plausible slip in the pre-pass: a rounding tie broken the wrong way, an
-exponent off by one, a scale factor or the sign diagonal dropped, the sign of an exact zero kept, V rotated too, the per-tensor
-amax taken over one block, the scale floor lost or not shifted for K.  The altered source is
-loaded as a module of its own and the pins of tests/test_fp8_oracle.py are run against it; the
-test passes only if some pin rejects it.
+exponent off by one, a scale factor or the sign diagonal dropped, the sign of an exact zero
+kept, V rotated too, the per-tensor amax taken over one block or one sequence, packed
+sequences quantised on blocks of the packed axis, the scale floor lost or not shifted for K.
+The altered source is loaded as a module of its own and the pins of tests/test_fp8_oracle.py
+are run against it; the test passes only if some pin rejects it.
 """
 import importlib.util
 import inspect
@@ -31,6 +32,12 @@ MUTATIONS = {
         "exps[b, h, j] = max(block_exponent(float(np.max(np.abs(blk))) if blk.size else 0.0), e_floor)",
         "exps[b, h, j] = block_exponent(float(np.max(np.abs(blk))) if blk.size else 0.0)"),
     "k_floor_not_shifted": ("SCALE_EXP_MIN + shift_k)", "SCALE_EXP_MIN)"),
+    "varlen_tensor_amax_from_first_sequence": (
+        "e_tensor = max(block_exponent(float(np.max(np.abs(y))) if y.size else 0.0), floor)",
+        "e_tensor = max(block_exponent(float(np.max(np.abs(y[:cu[1]])))), floor)"),
+    "varlen_blocks_not_restarted": ("c, e = quantize_blocks(seq, block, floor)",
+                                    "c, e = quantize_blocks(y[None, :cu[b + 1]], block, floor)\n"
+                                    "                c = c[:, cu[b]:]"),
     "signed_zero_kept": ("-int(exps[b, h, j])) + 0.0)", "-int(exps[b, h, j])))"),
     "dequantize_next_block": ("tok_blk = np.arange(N) // block", "tok_blk = np.minimum(np.arange(N) // block + 1, "
                               "scales.shape[2] - 1)"),

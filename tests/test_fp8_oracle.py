@@ -207,6 +207,50 @@ def test_scale_floor(per_tensor):
         assert v8[0, t, 0].tolist() == [_exact_code(z * Fraction(2) ** 126) for z in row]
 
 
+@pytest.mark.parametrize("per_tensor", [False, True])
+def test_varlen_prepare_is_per_sequence(per_tensor):
+    """Packed sequences quantise as independent dense runs: each sequence's codes and block
+    scales equal the dense pre-pass of that sequence alone (per block), or of that sequence
+    with the whole packed tensor's exponent (per tensor); a single sequence is the dense case."""
+    rng = np.random.default_rng(12)
+    lengths = [70, 1, 128, 200]
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    T, Hq, Hkv, d = int(cu[-1]), 4, 2, 16
+    scale_q = np.exp(rng.uniform(-3, 3, (T, 1, 1)))  # several exponents per sequence
+    q = bf16_to_f64(seeded_inputs.f32_to_bf16_bits((rng.standard_normal((T, Hq, d)) * scale_q).astype(np.float32)))
+    k = bf16_to_f64(seeded_inputs.f32_to_bf16_bits(rng.standard_normal((T, Hkv, d)).astype(np.float32)))
+    v = bf16_to_f64(seeded_inputs.f32_to_bf16_bits(rng.standard_normal((T, Hkv, d)).astype(np.float32)))
+    signs = seeded_inputs.hadamard_signs(d, seed=3)
+    got = fp8.fp8_prepare_varlen(q, k, v, cu, 256, signs, per_tensor=per_tensor)
+    assert got[3].shape == (4, Hq, 4) and got[4].shape == (4, Hkv, 4)
+    for b, n in enumerate(lengths):
+        sl = slice(cu[b], cu[b + 1])
+        want = fp8.fp8_prepare(q[None, sl], k[None, sl], v[None, sl], signs)
+        nb = -(-n // 64)
+        for i in range(3):
+            if per_tensor:
+                assert len(np.unique(got[3 + i])) == 1
+            else:
+                assert np.array_equal(got[i][sl], want[i][0]), (b, i)
+                assert np.array_equal(got[3 + i][b, :, :nb], want[3 + i][0]), (b, i)
+                assert np.all(np.isnan(got[3 + i][b, :, nb:]))
+    if per_tensor:  # per tensor: the dense pre-pass of the whole packed tensor as one sequence
+        dense = fp8.fp8_prepare(q[None], k[None], v[None], signs, per_tensor=True)
+        for i in range(3):
+            assert np.array_equal(got[i], dense[i][0])
+            assert got[3 + i].flat[0] == dense[3 + i].flat[0]
+    # dequantisation per sequence, and a single sequence is the dense case
+    dq = fp8.dequantize_varlen(got[0], got[3], cu)
+    for b in range(4):
+        sl = slice(cu[b], cu[b + 1])
+        nb = -(-lengths[b] // 64)
+        assert np.array_equal(dq[sl], fp8.dequantize(got[0][None, sl], got[3][b:b + 1, :, :nb])[0])
+    one = fp8.fp8_prepare_varlen(q[:70], k[:70], v[:70], [0, 70], 70, signs, per_tensor=per_tensor)
+    ref = fp8.fp8_prepare(q[None, :70], k[None, :70], v[None, :70], signs, per_tensor=per_tensor)
+    for i in range(6):
+        assert np.array_equal(one[i], ref[i][0] if i < 3 else ref[i])
+
+
 def test_mixture_inputs_moments():
     """N(0,1) + N(0,100) * Bernoulli(1e-3): second moment 1 + 100 * 1e-3 = 1.1, and about
     1e-3 * P(|N(0,100)| > 8) = 1e-3 * 0.4237 of the elements exceed 8 in magnitude (a standard
