@@ -12,6 +12,8 @@ sweep's aggregate (total FLOPs over total time).  ``--workload`` selects the oth
   varlen  bf16 causal GQA (Hq=32, Hkv=8, d=128), 8 packed sequences of 256..8192 tokens
   fp8     e4m3 non-causal B=2 H=16 N=8192 d=128 on pre-quantised inputs; the FP8 pre-pass
           (Hadamard rotation + block quantisation, HBM-bound) is timed separately
+  fp8_causal  the same kernel causal, on the bf16 causal d=128 workload's inputs
+  fp8_varlen  the same kernel on the packed causal GQA workload's inputs
   ceiling the matrix-core ceiling the attention kernels run against: back-to-back
           v_mfma_f32_32x32x16_bf16 on random operands on every CU (2 and 4 waves per SIMD),
           with no LDS or vector-ALU work; under the chip's power limit this sits well below
@@ -75,7 +77,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="mha16k", choices=["mha16k", "sweep", "causal", "varlen", "fp8", "ceiling"])
+    ap.add_argument("--workload", default="mha16k", choices=["mha16k", "sweep", "causal", "varlen", "fp8", "fp8_causal",
+                                                              "fp8_varlen", "ceiling"])
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -212,39 +215,52 @@ def run_16bit(args, name, inp, dev, stream, traffic=None, cpu=False):
                 launches=launches)
 
 
-def run_fp8(args, dev, stream):
+# FP8 workloads: name of the line -> the seeded bf16 inputs it quantises
+FP8_WORKLOADS = {"fp8": "fp8_b2_h16_n8192_d128", "fp8_causal": "causal_b2_h16_n8192_d128",
+                 "fp8_varlen": "gqa_varlen_causal_hq32_hkv8_d128"}
+
+
+def run_fp8(args, dev, stream, workload="fp8"):
     import torch
 
     import exact_attention_76_amd as ea
     import seeded_inputs as si
 
-    inp = si.CONFIGS["fp8_b2_h16_n8192_d128"]()
+    src = FP8_WORKLOADS[workload]
+    inp = si.CONFIGS[src]()
     q, k, v = (to_dev(getattr(inp, n), "bf16", dev) for n in "qkv")
     signs = torch.from_numpy(si.hadamard_signs(inp.d)).to(dev)
-    q8, k8, v8, qs, ks, vs = ea.fp8_prepare(q, k, v, hadamard_signs=signs, stream=stream)
+    packed = {}
+    if inp.cu_seqlens is not None:
+        packed = dict(cu_seqlens=torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(dev), max_seqlen=inp.N)
+    q8, k8, v8, qs, ks, vs = ea.fp8_prepare(q, k, v, hadamard_signs=signs, stream=stream, **packed)
     o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((inp.B, inp.Hq, inp.N), dtype=torch.float32, device=dev)
+    lse_shape = (inp.B, inp.Hq, inp.N) if not packed else (inp.Hq, inp.total_tokens)
+    lse = torch.empty(lse_shape, dtype=torch.float32, device=dev)
 
     def attn():
-        ea.attn_fwd(q8, k8, v8, o, lse, alpha=inp.alpha, q_scale=qs, k_scale=ks, v_scale=vs, stream=stream)
+        ea.attn_fwd(q8, k8, v8, o, lse, causal=inp.causal, alpha=inp.alpha, q_scale=qs, k_scale=ks, v_scale=vs,
+                    stream=stream, **packed)
 
     def prep():
-        ea.attn_fp8_prepare(q, k, v, q8, k8, v8, qs, ks, vs, hadamard_signs=signs, stream=stream)
+        ea.attn_fp8_prepare_ex(q, k, v, q8, k8, v8, qs, ks, vs, hadamard_signs=signs, stream=stream, **packed)
 
     ms_wall, ms_gpu = timed(attn, stream, args.steps, args.warmup)
     launches = per_launch(attn, stream, args.steps)
     pw, pg = timed(prep, stream, args.steps, args.warmup)
-    nblk = -(-inp.N // 64)
-    prep_bytes = 3 * q.numel() * 2 + 3 * q.numel() + 3 * inp.B * inp.Hq * nblk * 4 + inp.d
-    extra = {"attention_only": True, "hadamard": True,
+    elems = q.numel() + k.numel() + v.numel()
+    prep_bytes = 2 * elems + elems + (qs.numel() + ks.numel() + vs.numel()) * 4 + inp.d
+    extra = {"attention_only": True, "hadamard": True, "inputs_from": src,
              "prepare_ms": round(pw, 4),
              "prepare_roofline": {"bound": "hbm", "achieved": round(prep_bytes / (pg * 1e-3) / 1e9, 1),
                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                   "frac": round(prep_bytes / (pg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                  "traffic": measured_traffic("fp8_prepare"), "bytes_per_launch": prep_bytes},
+                                  "traffic": measured_traffic("fp8_prepare") if workload == "fp8" else None,
+                                  "bytes_per_launch": prep_bytes},
              "prepare_plus_attention_tflops": round(inp.flops() / ((pw + ms_wall) * 1e-3) / 1e12, 2)}
-    return line(args, "fp8_b2_h16_n8192_d128", inp, inp.flops(), ms_wall, ms_gpu, "fp8", extra=extra,
-                traffic=measured_traffic("fp8_attention"), launches=launches)
+    name = "fp8_b2_h16_n8192_d128" if workload == "fp8" else f"fp8_{src}"
+    return line(args, name, inp, inp.flops(), ms_wall, ms_gpu, "fp8", extra=extra,
+                traffic=measured_traffic("fp8_attention") if workload == "fp8" else None, launches=launches)
 
 
 def run_ceiling(args, dev, stream):
@@ -339,8 +355,8 @@ def main():
         elif args.workload == "varlen":
             n = "gqa_varlen_causal_hq32_hkv8_d128"
             out = [run_16bit(args, n, si.CONFIGS[n](), dev, stream)]
-        elif args.workload == "fp8":
-            out = [run_fp8(args, dev, stream)]
+        elif args.workload in FP8_WORKLOADS:
+            out = [run_fp8(args, dev, stream, args.workload)]
         else:
             out = run_ceiling(args, dev, stream)
     for o in out:

@@ -9,7 +9,8 @@ Entry points carry the names of the C ABI:
 * :func:`attn_fwd` -- O and LSE of exact attention (bf16 / fp16 / fp8-e4m3 inputs; dense or
   packed variable-length; causal or not; grouped-query heads).
 * :func:`attn_fp8_prepare` -- Hadamard rotation + per-block power-of-two e4m3 quantisation.
-* :func:`attn_fp8_prepare_scaling` -- the same with a choice of per-block or per-tensor scales.
+* :func:`attn_fp8_prepare_ex` -- the same for packed sequences too, with per-block or per-tensor
+  scales.
 * :func:`attn_strerror` -- text of a status code.
 
 Helpers :func:`attention` and :func:`fp8_prepare` allocate the outputs and call the above.
@@ -22,7 +23,7 @@ import re
 
 import torch
 
-__all__ = ["AttnError", "attn_fwd", "attn_fp8_prepare", "attn_fp8_prepare_scaling", "attn_strerror", "attention",
+__all__ = ["AttnError", "attn_fwd", "attn_fp8_prepare", "attn_fp8_prepare_ex", "attn_strerror", "attention",
            "fp8_prepare", "load_library", "LIB_PATH", "ATTN_BF16", "ATTN_FP16", "ATTN_FP8_E4M3",
            "ATTN_FP8_SCALE_BLOCK", "ATTN_FP8_SCALE_TENSOR"]
 
@@ -60,8 +61,8 @@ def load_library(build_if_missing: bool = True):
     lib.attn_fwd.restype = I
     lib.attn_fp8_prepare.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, P]
     lib.attn_fp8_prepare.restype = I
-    lib.attn_fp8_prepare_scaling.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, I, P]
-    lib.attn_fp8_prepare_scaling.restype = I
+    lib.attn_fp8_prepare_ex.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, P, I, P, I, P]
+    lib.attn_fp8_prepare_ex.restype = I
     lib.attn_strerror.argtypes = [I]
     lib.attn_strerror.restype = ctypes.c_char_p
     _lib = lib
@@ -201,8 +202,8 @@ def attention(q, k, v, *, causal: bool = False, alpha: float | None = None, cu_s
     return o, lse
 
 
-def _prepare_call(q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, hadamard_signs, name):
-    """Check the pre-pass tensors; return the device and the C arguments before the mode."""
+def _prepare_call(q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, hadamard_signs, cu_seqlens, max_seqlen, name):
+    """Check the pre-pass tensors; return the device and (B, Hq, Hkv, N, d)."""
     for nm, t in (("q", q), ("k", k), ("v", v), ("q8", q8), ("k8", k8), ("v8", v8),
                   ("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
         _check_tensor(t, nm)
@@ -212,11 +213,25 @@ def _prepare_call(q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, hadamard_signs
             raise TypeError("hadamard_signs must be int8")
     if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
         raise TypeError(f"{name} takes bf16 inputs")
-    B, N, Hq, d = q.shape
-    Hkv = k.shape[2]
+    if cu_seqlens is None:
+        if q.dim() != 4:
+            raise ValueError("dense q must be [B, N, Hq, d]")
+        B, N, Hq, d = q.shape
+        Hkv = k.shape[2]
+        kv_shape = (B, N, Hkv, d)
+    else:
+        _check_tensor(cu_seqlens, "cu_seqlens")
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+        if q.dim() != 3 or max_seqlen is None:
+            raise ValueError("packed q must be [T, Hq, d] and max_seqlen must be given")
+        B, N = cu_seqlens.numel() - 1, int(max_seqlen)
+        T, Hq, d = q.shape
+        Hkv = k.shape[1]
+        kv_shape = (T, Hkv, d)
     nblk = -(-N // 64)
-    if tuple(k.shape) != (B, N, Hkv, d) or tuple(v.shape) != (B, N, Hkv, d):
-        raise ValueError("k and v must be [B, N, Hkv, d] like q")
+    if tuple(k.shape) != kv_shape or tuple(v.shape) != kv_shape:
+        raise ValueError(f"k and v must be {kv_shape}")
     for t, ref in ((q8, q), (k8, k), (v8, v)):
         if tuple(t.shape) != tuple(ref.shape) or t.element_size() != 1:
             raise ValueError("fp8 outputs must be 1-byte tensors shaped like their inputs")
@@ -226,42 +241,54 @@ def _prepare_call(q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, hadamard_signs
     if hadamard_signs is not None and hadamard_signs.numel() != d:
         raise ValueError("hadamard_signs must have d entries")
     dev = _one_device((("q", q), ("k", k), ("v", v), ("q8", q8), ("k8", k8), ("v8", v8), ("q_scale", q_scale),
-                       ("k_scale", k_scale), ("v_scale", v_scale), ("hadamard_signs", hadamard_signs)))
-    args = (_ptr(q), _ptr(k), _ptr(v), _ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
-            B, Hq, Hkv, N, d, _ptr(hadamard_signs))
-    return dev, args
+                       ("k_scale", k_scale), ("v_scale", v_scale), ("hadamard_signs", hadamard_signs),
+                       ("cu_seqlens", cu_seqlens)))
+    return dev, (B, Hq, Hkv, N, d)
 
 
 def attn_fp8_prepare(q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, *, hadamard_signs=None,
                      stream=None) -> None:
     """Enqueue the FP8 pre-pass: bf16 q/k/v [B, N, H, d] -> e4m3 codes + fp32 block scales
     [B, H, ceil(N/64)].  ``hadamard_signs``: int8 [d] of +-1 on the GPU, or None for no rotation."""
-    dev, args = _prepare_call(q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, hadamard_signs, "attn_fp8_prepare")
+    dev, (B, Hq, Hkv, N, d) = _prepare_call(q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, hadamard_signs,
+                                            None, None, "attn_fp8_prepare")
     lib = load_library()
     with torch.cuda.device(dev):
-        st = lib.attn_fp8_prepare(*args, _stream_handle(stream, dev))
+        st = lib.attn_fp8_prepare(_ptr(q), _ptr(k), _ptr(v), _ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale),
+                                  _ptr(k_scale), _ptr(v_scale), B, Hq, Hkv, N, d, _ptr(hadamard_signs),
+                                  _stream_handle(stream, dev))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fp8_prepare")
 
 
-def attn_fp8_prepare_scaling(q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, *, scaling: int,
-                             hadamard_signs=None, stream=None) -> None:
-    """:func:`attn_fp8_prepare` with ``scaling`` = ATTN_FP8_SCALE_BLOCK (one scale per 64-token
-    block) or ATTN_FP8_SCALE_TENSOR (one scale per tensor, repeated in every block entry)."""
-    dev, args = _prepare_call(q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, hadamard_signs,
-                              "attn_fp8_prepare_scaling")
+def attn_fp8_prepare_ex(q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, *, scaling: int = ATTN_FP8_SCALE_BLOCK,
+                        cu_seqlens=None, max_seqlen: int | None = None, hadamard_signs=None, stream=None) -> None:
+    """:func:`attn_fp8_prepare` for the dense or the packed layout (``cu_seqlens`` int32 [B+1]
+    on the GPU, q [T, Hq, d], k/v [T, Hkv, d], ``max_seqlen`` >= the longest sequence; scales
+    [B, H, ceil(max_seqlen/64)]), with ``scaling`` = ATTN_FP8_SCALE_BLOCK (one scale per
+    64-token block) or ATTN_FP8_SCALE_TENSOR (one scale per tensor, in every block entry)."""
+    dev, (B, Hq, Hkv, N, d) = _prepare_call(q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, hadamard_signs,
+                                            cu_seqlens, max_seqlen, "attn_fp8_prepare_ex")
     lib = load_library()
     with torch.cuda.device(dev):
-        st = lib.attn_fp8_prepare_scaling(*args, int(scaling), _stream_handle(stream, dev))
+        st = lib.attn_fp8_prepare_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale),
+                                     _ptr(k_scale), _ptr(v_scale), B, Hq, Hkv, N, _ptr(cu_seqlens), d,
+                                     _ptr(hadamard_signs), int(scaling), _stream_handle(stream, dev))
     if st != ATTN_OK:
-        raise AttnError(st, "attn_fp8_prepare_scaling")
+        raise AttnError(st, "attn_fp8_prepare_ex")
 
 
-def fp8_prepare(q, k, v, *, hadamard_signs=None, per_tensor: bool = False, stream=None):
+def fp8_prepare(q, k, v, *, hadamard_signs=None, per_tensor: bool = False, cu_seqlens=None,
+                max_seqlen: int | None = None, stream=None):
     """Allocate the e4m3 tensors (as uint8 codes) and scales and run the pre-pass, with one scale
-    per 64-token block (:func:`attn_fp8_prepare`) or, with ``per_tensor``, one per tensor."""
-    B, N, Hq, d = q.shape
-    Hkv = k.shape[2]
+    per 64-token block (:func:`attn_fp8_prepare`) or, with ``per_tensor``, one per tensor;
+    ``cu_seqlens`` / ``max_seqlen`` select the packed layout (:func:`attn_fp8_prepare_ex`)."""
+    if cu_seqlens is None:
+        B, N, Hq, d = q.shape
+        Hkv = k.shape[2]
+    else:
+        B, N = cu_seqlens.numel() - 1, int(max_seqlen)
+        Hq, Hkv = q.shape[1], k.shape[1]
     nblk = -(-N // 64)
     dev = q.device
     q8 = torch.empty(q.shape, dtype=torch.uint8, device=dev)
@@ -270,9 +297,11 @@ def fp8_prepare(q, k, v, *, hadamard_signs=None, per_tensor: bool = False, strea
     qs = torch.empty((B, Hq, nblk), dtype=torch.float32, device=dev)
     ks = torch.empty((B, Hkv, nblk), dtype=torch.float32, device=dev)
     vs = torch.empty((B, Hkv, nblk), dtype=torch.float32, device=dev)
-    if per_tensor:
-        attn_fp8_prepare_scaling(q, k, v, q8, k8, v8, qs, ks, vs, scaling=ATTN_FP8_SCALE_TENSOR,
-                                 hadamard_signs=hadamard_signs, stream=stream)
+    if per_tensor or cu_seqlens is not None:
+        attn_fp8_prepare_ex(q, k, v, q8, k8, v8, qs, ks, vs,
+                            scaling=ATTN_FP8_SCALE_TENSOR if per_tensor else ATTN_FP8_SCALE_BLOCK,
+                            cu_seqlens=cu_seqlens, max_seqlen=max_seqlen, hadamard_signs=hadamard_signs,
+                            stream=stream)
     else:
         attn_fp8_prepare(q, k, v, q8, k8, v8, qs, ks, vs, hadamard_signs=hadamard_signs, stream=stream)
     return q8, k8, v8, qs, ks, vs

@@ -34,6 +34,7 @@
 
 #include <type_traits>
 
+#include "decompose.h"
 #include "internal.h"
 
 namespace attn {
@@ -83,56 +84,6 @@ __device__ __forceinline__ float halves_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-
-// Bijection from hardware workgroup id to a logical id such that each XCD (hardware id mod 8)
-// receives one contiguous range of logical ids.
-__device__ __forceinline__ int xcd_remap(int wg, int total) {
-  constexpr int kXcd = 8;
-  const int q = total / kXcd, r = total % kXcd;
-  const int x = wg % kXcd, i = wg / kXcd;
-  return x * q + (x < r ? x : r) + i;
-}
-
-// Work decomposition: hardware workgroup id -> (query block, head, sequence).  Workgroups are
-// dispatched round-robin over the 8 XCDs (id mod 8), each XCD running its share in id order.
-// When the heads split evenly over the XCDs, every XCD owns the same heads of every sequence,
-// so packed sequences of unequal length load all XCDs alike; whole KV groups stay on one XCD
-// (their query heads share the group's K/V in that XCD's L2) when the KV heads split evenly too.
-// Inside an XCD, causal grids run all query blocks longest first (a block's work grows with
-// its index); non-causal grids keep the blocks of one head together.  Otherwise each XCD
-// takes one contiguous range of (sequence, head, block) ids, causal blocks longest first.
-template <bool CAUSAL>
-__device__ __forceinline__ void decompose(int wg, int nqb, int Hq, int Hkv, int B, int& qb, int& h, int& b) {
-  constexpr int kXcd = 8;
-  if (Hq % kXcd == 0) {
-    const int x = wg % kXcd, slot = wg / kXcd;
-    const int hpx = Hq / kXcd;  // heads per XCD and sequence
-    int r;
-    if (CAUSAL) {
-      qb = nqb - 1 - slot / (hpx * B);
-      r = slot % (hpx * B);
-    } else {
-      qb = slot % nqb;
-      r = slot / nqb;
-    }
-    b = r / hpx;
-    const int hh = r % hpx;
-    if (Hkv % kXcd == 0) {
-      const int G = Hq / Hkv;  // query heads per KV group; groups x, x + 8, ... live on XCD x
-      h = (x + kXcd * (hh / G)) * G + hh % G;
-    } else {
-      h = x + kXcd * hh;
-    }
-  } else {
-    const int logical = xcd_remap(wg, nqb * Hq * B);
-    qb = logical % nqb;
-    const int bh = logical / nqb;
-    h = bh % Hq;
-    b = bh / Hq;
-    if (CAUSAL) qb = nqb - 1 - qb;
-  }
-}
-
 
 // ---- LDS tile layout -------------------------------------------------------------------------
 // A K or V tile of BC rows x D columns (16-bit) is stored as blocks of 16 rows; inside a block

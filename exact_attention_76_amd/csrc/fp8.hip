@@ -18,9 +18,10 @@
 //     workgroup per tensor reduces the slots to the tensor's exponent and writes its scale
 //     everywhere, and the kernel runs again with that exponent.  Every scale is kept at
 //     2^-126 or more, a normal fp32 whose exponent is the E8M0 operand the attention uses.
-//   * Attention: the plain loop of the 16-bit kernel (scores formed transposed, online softmax
-//     in fp32, K/V tiles copied buffer-to-LDS, two LDS stages, one barrier per tile) with four
-//     waves (128 queries) per workgroup and three workgroups per CU -- the softmax is the larger
+//   * Attention (dense or packed sequences, causal or not, grouped-query heads): the plain loop
+//     of the 16-bit kernel (scores formed transposed, online softmax in fp32, K/V tiles copied
+//     buffer-to-LDS, two LDS stages, one barrier per tile) with four waves (128 queries) per
+//     workgroup and three workgroups per CU -- the softmax is the larger
 //     share here, and three waves per SIMD hide it better than two in a ping-pong -- and both
 //     products on v_mfma_scale_f32_32x32x64_f8f6f4.  The per-block power-of-two scales of
 //     Q, K and V go into the instruction's E8M0 scale operands, so they cost nothing.  P is
@@ -32,6 +33,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "decompose.h"
 #include "internal.h"
 
 namespace attn {
@@ -93,9 +95,12 @@ enum PrepPass : int {
   kPrepTensorCodes = 2,  // per-tensor, last pass: codes with the exponent the slot now holds
 };
 
+// Dense: B sequences of N tokens.  Packed (cu != nullptr): sequence b holds tokens cu[b] ..
+// cu[b+1]-1 (at most N of them), and its blocks count from its first token.
 template <int PASS>
 __global__ __launch_bounds__(256) void fp8_prepare_kernel(PrepTensor t0, PrepTensor t1, PrepTensor t2, int B, int N,
-                                                          int nblk, const signed char* __restrict__ signs) {
+                                                          int nblk, const int* __restrict__ cu,
+                                                          const signed char* __restrict__ signs) {
   const PrepTensor t = blockIdx.y == 0 ? t0 : (blockIdx.y == 1 ? t1 : t2);
   const int H = t.H;
   if ((int)blockIdx.x >= B * H * nblk) return;  // this tensor has fewer heads than the grid
@@ -103,10 +108,20 @@ __global__ __launch_bounds__(256) void fp8_prepare_kernel(PrepTensor t0, PrepTen
   const int bh = blockIdx.x / nblk;
   const int h = bh % H, b = bh / H;
   const int tid = threadIdx.x;
+  float* const slot = t.scale + ((int64_t)b * H + h) * nblk + blk;
+  int seq_start = b * N, n = N;
+  if (cu != nullptr) {
+    seq_start = cu[b];
+    n = min(cu[b + 1] - seq_start, N);
+    if (blk * 64 >= n) {  // past the end of this sequence: no codes; the scan leaves no exponent
+      if (PASS == kPrepTensorScan && tid == 0) *slot = __int_as_float(INT_MIN);
+      return;
+    }
+  }
   const int r = tid >> 2, p = tid & 3;  // token row of the block, quarter of the 128 features
   const int token = blk * 64 + r;
-  const bool valid = token < N;
-  const int64_t rowoff = ((int64_t)b * N + (valid ? token : 0)) * H + h;
+  const bool valid = token < n;
+  const int64_t rowoff = ((int64_t)seq_start + (valid ? token : 0)) * H + h;
 
   double y[32];
   {
@@ -146,7 +161,6 @@ __global__ __launch_bounds__(256) void fp8_prepare_kernel(PrepTensor t0, PrepTen
       }
     }
   }
-  float* const slot = t.scale + ((int64_t)b * H + h) * nblk + blk;
   int e;
   if constexpr (PASS == kPrepTensorCodes) {
     e = (int)((__float_as_uint(*slot) >> 23) & 0xFF) - 127 + t.scale_shift;  // slot holds 2^(e - shift)
@@ -263,24 +277,20 @@ __device__ __forceinline__ float halves_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-__device__ __forceinline__ int xcd_remap(int wg, int total) {
-  constexpr int kXcd = 8;
-  const int q = total / kXcd, r = total % kXcd;
-  const int x = wg % kXcd, i = wg / kXcd;
-  return x * q + (x < r ? x : r) + i;
-}
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   f32x2 v = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // WAVES waves of 32 queries per workgroup; BC keys per tile (64 or 128, a multiple of the
-// 64-token scale block).
-template <int WAVES, int BC>
+// 64-token scale block).  CAUSAL: key j visible to query i iff j <= i.  VARLEN: packed sequences
+// [T, H, d] delimited by cu_seqlens, scale blocks counted from each sequence's first token.
+template <int WAVES, int BC, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 3 : 1)) void fwd_fp8_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
     const float* __restrict__ qs, const float* __restrict__ ks_, const float* __restrict__ vs_,
-    uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int N, float alpha, int num_qblocks) {
+    uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int N, const int* __restrict__ cu_seqlens,
+    int nseq, float alpha, int num_qblocks) {
   constexpr int BR = 32 * WAVES;        // queries per workgroup
   constexpr int TILE = BC * kD;         // bytes of one K or V tile
   constexpr int NI = TILE / 1024 / WAVES;  // 1 KB copies per wave per tensor
@@ -296,11 +306,17 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 3 : 1)) void fwd_fp8_kern
   const int l32 = lane & 31, hi = lane >> 5;
   const int nblk = (N + 63) / 64;
 
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int qb = logical % num_qblocks;
-  const int bh = logical / num_qblocks;
-  const int h = bh % Hq, b = bh / Hq;
-  const int n = N, seq_start = b * N;
+  int qb, h, b;
+  decompose<CAUSAL>(blockIdx.x, num_qblocks, Hq, Hkv, nseq, qb, h, b);
+  int seq_start, n;
+  if constexpr (VARLEN) {
+    seq_start = cu_seqlens[b];
+    n = cu_seqlens[b + 1] - seq_start;
+    if (n > N) n = N;
+  } else {
+    seq_start = b * N;
+    n = N;
+  }
   const int q0 = qb * BR;
   const int g = h / (Hq / Hkv);
   const int qw = q0 + wave * 32;
@@ -359,7 +375,8 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 3 : 1)) void fwd_fp8_kern
   float m = -INFINITY;
   float l = 0.f;
   const float c = alpha * kLog2e;
-  const int ntiles = (n + BC - 1) / BC;
+  const int kv_end = CAUSAL ? min(n, q0 + BR) : n;  // keys any query of the workgroup sees
+  const int ntiles = (kv_end + BC - 1) / BC;
 
   auto compute_tile = [&](const char* stage, int j) {
     const char* kt = stage;
@@ -378,12 +395,14 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 3 : 1)) void fwd_fp8_kern
         s[cb] = mma_f8(a, qf[st], s[cb], sk, sq);
       }
     }
-    if (k0 + BC > n) {
+    if (k0 + BC > n || (CAUSAL && k0 + BC - 1 > qw)) {
 #pragma unroll
       for (int cb = 0; cb < NB_C; ++cb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (k0 + cb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3) >= n) s[cb][r] = -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + cb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+          if (key >= n || (CAUSAL && key > qi)) s[cb][r] = -INFINITY;
+        }
     }
     float mt = -INFINITY;
 #pragma unroll
@@ -445,14 +464,16 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 3 : 1)) void fwd_fp8_kern
   issue_tile(st0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  // causal: a wave skips the tiles that lie wholly above its diagonal (its first tile always has
+  // visible keys, so its running maximum is finite from then on); it still copies and waits
   for (int j = 0; j < ntiles; j += 2) {
     if (j + 1 < ntiles) issue_tile(st1, j + 1);
-    compute_tile(st0, j);
+    if (!CAUSAL || j * BC <= qw + 31) compute_tile(st0, j);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (j + 1 >= ntiles) break;
     if (j + 2 < ntiles) issue_tile(st0, j + 2);
-    compute_tile(st1, j + 1);
+    if (!CAUSAL || (j + 1) * BC <= qw + 31) compute_tile(st1, j + 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
@@ -471,7 +492,8 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 3 : 1)) void fwd_fp8_kern
       }
     if (hi == 0) {
       // l carries the factor 2^8 of P'
-      lse[((int64_t)b * Hq + h) * N + qi] = lt > 0.f ? m * alpha + __logf(lt) - 8.f * kLn2 : -INFINITY;
+      const int64_t idx = VARLEN ? (int64_t)h * cu_seqlens[nseq] + seq_start + qi : ((int64_t)b * Hq + h) * N + qi;
+      lse[idx] = lt > 0.f ? m * alpha + __logf(lt) - 8.f * kLn2 : -INFINITY;
     }
   }
 }
@@ -492,32 +514,39 @@ hipError_t launch_fp8_prepare(const PrepareArgs& a, hipStream_t stream) {
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (!a.per_tensor) {
     hipLaunchKernelGGL(fp8_prepare_kernel<kPrepBlock>, dim3((unsigned)grid, 3), dim3(256), 0, stream, tq, tk, tv, a.B,
-                       a.N, nblk, a.signs);
+                       a.N, nblk, a.cu_seqlens, a.signs);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(fp8_prepare_kernel<kPrepTensorScan>, dim3((unsigned)grid, 3), dim3(256), 0, stream, tq, tk, tv,
-                     a.B, a.N, nblk, a.signs);
+                     a.B, a.N, nblk, a.cu_seqlens, a.signs);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(fp8_tensor_scale_kernel, dim3(3), dim3(1024), 0, stream, tq, tk, tv, a.B, nblk);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(fp8_prepare_kernel<kPrepTensorCodes>, dim3((unsigned)grid, 3), dim3(256), 0, stream, tq, tk, tv,
-                     a.B, a.N, nblk, a.signs);
+                     a.B, a.N, nblk, a.cu_seqlens, a.signs);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream) {
+template <bool CAUSAL, bool VARLEN>
+hipError_t launch_fp8_mode(const FwdArgs& a, hipStream_t stream) {
   constexpr int kWaves = [] { int w[] = {ATTN_FP8_SHAPE}; return w[0]; }();
   const int br = 32 * kWaves;
   const int nqb = (a.N + br - 1) / br;
   const long long grid = (long long)nqb * a.Hq * a.B;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_fp8_kernel<ATTN_FP8_SHAPE>), dim3((unsigned)grid), dim3(64 * kWaves), 0, stream,
-                     static_cast<const uint8_t*>(a.q), static_cast<const uint8_t*>(a.k),
+  hipLaunchKernelGGL((fwd_fp8_kernel<ATTN_FP8_SHAPE, CAUSAL, VARLEN>), dim3((unsigned)grid), dim3(64 * kWaves), 0,
+                     stream, static_cast<const uint8_t*>(a.q), static_cast<const uint8_t*>(a.k),
                      static_cast<const uint8_t*>(a.v), a.q_scale, a.k_scale, a.v_scale,
-                     static_cast<uint16_t*>(a.o), a.lse, a.Hq, a.Hkv, a.N, a.alpha, nqb);
+                     static_cast<uint16_t*>(a.o), a.lse, a.Hq, a.Hkv, a.N, a.cu_seqlens, a.B, a.alpha, nqb);
   return hipGetLastError();
+}
+
+hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream) {
+  const bool varlen = a.cu_seqlens != nullptr;
+  if (a.causal) return varlen ? launch_fp8_mode<true, true>(a, stream) : launch_fp8_mode<true, false>(a, stream);
+  return varlen ? launch_fp8_mode<false, true>(a, stream) : launch_fp8_mode<false, false>(a, stream);
 }
 
 }  // namespace attn

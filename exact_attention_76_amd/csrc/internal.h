@@ -26,7 +26,7 @@ struct FwdArgs {
 // 16-bit inputs (bf16 when is_bf16, else fp16); d in {64, 128, 256}.
 hipError_t launch_fwd_16bit(const FwdArgs& a, bool is_bf16, hipStream_t stream);
 
-// e4m3 inputs with per-block scales; d == 128, dense, non-causal.
+// e4m3 inputs with per-block scales; d == 128; dense or packed, causal or not.
 hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream);
 
 struct PrepareArgs {
@@ -39,7 +39,8 @@ struct PrepareArgs {
   float* q_scale;
   float* k_scale;
   float* v_scale;
-  int B, Hq, Hkv, N, d;
+  int B, Hq, Hkv, N, d;       // N: sequence length (dense) or longest sequence (packed)
+  const int* cu_seqlens;      // device int32 [B+1] or nullptr
   const signed char* signs;
   int per_tensor;             // one scale per tensor instead of one per 64-token block
 };

@@ -75,9 +75,10 @@ enum {
  * q_scale, k_scale, v_scale (ATTN_FP8_E4M3 only, else ignored): fp32 device arrays of
  *   powers of two, [B, Hq, ceil(N/64)] for q and [B, Hkv, ceil(N/64)] for k and v; block c
  *   covers tokens 64c .. 64c+63 of a (batch, head).  The attention inputs are
- *   e4m3(x) * scale (digest section 3.5, block quantisation).  Each scale must be a normal
- *   fp32 power of two, 2^-126 .. 2^127: the kernel passes its exponent to the matrix
- *   instruction as an E8M0 scale.  FP8 currently requires the dense layout and causal == 0.
+ *   e4m3(x) * scale (digest section 3.5, block quantisation).  In the packed layout, b is
+ *   the sequence and block c covers tokens 64c .. 64c+63 counted from the sequence's first
+ *   token.  Each scale must be a normal fp32 power of two, 2^-126 .. 2^127: the kernel
+ *   passes its exponent to the matrix instruction as an E8M0 scale.
  * lse:     fp32, natural log, in units of the scaled scores S.  A row without visible keys
  *          gets O = 0 and L = -inf.
  *
@@ -127,24 +128,31 @@ typedef enum {
 } attn_fp8_scaling_t;
 
 /*
- * attn_fp8_prepare_scaling -- attn_fp8_prepare with a choice of scale granularity.
+ * attn_fp8_prepare_ex -- attn_fp8_prepare with every option: the packed variable-length
+ * layout and a choice of scale granularity.
  *
- * ATTN_FP8_SCALE_BLOCK is exactly attn_fp8_prepare.  ATTN_FP8_SCALE_TENSOR is per-tensor
- * scaling, the usual practice that the digest's section 3.5 contrasts with block quantisation
- * and the baseline of the FlashAttention-3 paper's FP8 error ablation (section 4.3, Table 3):
- * e is chosen by the same rule from the largest magnitude of the whole (rotated) tensor, all
- * batches and heads, and that one scale is written into every [b, h, block] entry, so the
- * outputs feed attn_fwd unchanged.  The per-tensor pre-pass takes three kernel launches on
- * `stream` and uses the scale arrays as working storage between them: their contents are
- * defined only once all three have run.  Any other value of `scaling` returns
- * ATTN_ERR_INVALID.  Arguments, layouts and errors are otherwise those of attn_fp8_prepare.
+ * cu_seqlens: NULL for the dense layout, or the packed layout of attn_fwd: int32 [B + 1] on the
+ *   device, q [T, Hq, d], k and v [T, Hkv, d], N >= the longest sequence.  Blocks then count
+ *   from each sequence's first token, so every sequence is quantised as it would be alone;
+ *   the scales are [B, H, ceil(N/64)], and entries past a sequence's last block are not
+ *   defined (attn_fwd never reads them).
+ * scaling: ATTN_FP8_SCALE_BLOCK is attn_fp8_prepare's rule.  ATTN_FP8_SCALE_TENSOR is
+ *   per-tensor scaling, the usual practice that the digest's section 3.5 contrasts with block
+ *   quantisation and the baseline of the FlashAttention-3 paper's FP8 error ablation (section
+ *   4.3, Table 3): e is chosen by the same rule from the largest magnitude of the whole
+ *   (rotated) tensor, all batches, sequences and heads, and that one scale is written into
+ *   every [b, h, block] entry, so the outputs feed attn_fwd unchanged.  The per-tensor pre-pass
+ *   takes three kernel launches on `stream` and uses the scale arrays as working storage
+ *   between them: their contents are defined only once all three have run.  Any other value
+ *   returns ATTN_ERR_INVALID.
+ * Everything else is as for attn_fp8_prepare.
  */
-int attn_fp8_prepare_scaling(const void* q, const void* k, const void* v,
-                             void* q8, void* k8, void* v8,
-                             float* q_scale, float* k_scale, float* v_scale,
-                             int B, int Hq, int Hkv, int N, int d,
-                             const signed char* hadamard_signs, attn_fp8_scaling_t scaling,
-                             hipStream_t stream);
+int attn_fp8_prepare_ex(const void* q, const void* k, const void* v,
+                        void* q8, void* k8, void* v8,
+                        float* q_scale, float* k_scale, float* v_scale,
+                        int B, int Hq, int Hkv, int N, const int* cu_seqlens, int d,
+                        const signed char* hadamard_signs, attn_fp8_scaling_t scaling,
+                        hipStream_t stream);
 
 /* Static description of a status code. */
 const char* attn_strerror(int status);

@@ -19,7 +19,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = ea.header_functions()
-    assert set(names) == {"attn_fwd", "attn_fp8_prepare", "attn_fp8_prepare_scaling", "attn_strerror"}
+    assert set(names) == {"attn_fwd", "attn_fp8_prepare", "attn_fp8_prepare_ex", "attn_strerror"}
     out = subprocess.run(["nm", "-D", "--defined-only", ea.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
@@ -71,8 +71,8 @@ def fwd(lib, q=A, k=A, v=A, o=A, lse=A, B=1, Hq=2, Hkv=2, N=128, cu=None, d=128,
     (dict(dtype=ea.ATTN_FP8_E4M3), ea.ATTN_ERR_INVALID),  # no scales
     (dict(dtype=ea.ATTN_FP8_E4M3, qs=A, ks=A), ea.ATTN_ERR_INVALID),
     (dict(dtype=ea.ATTN_FP8_E4M3, qs=A, ks=A, vs=A, d=64), ea.ATTN_ERR_UNSUPPORTED),
-    (dict(dtype=ea.ATTN_FP8_E4M3, qs=A, ks=A, vs=A, cu=A), ea.ATTN_ERR_UNSUPPORTED),
-    (dict(dtype=ea.ATTN_FP8_E4M3, qs=A, ks=A, vs=A, causal=1), ea.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=ea.ATTN_FP8_E4M3, qs=A, ks=A, vs=A, cu=A, d=256), ea.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=ea.ATTN_FP8_E4M3, qs=A, ks=A, vs=A, causal=1, q=A + 4), ea.ATTN_ERR_ALIGN),
 ])
 def test_fwd_validation(lib, kw, status):
     assert fwd(lib, **kw) == status
@@ -98,11 +98,11 @@ def test_prepare_validation(lib, kw, status):
     assert prep(lib, **kw) == status
 
 
-def prep_scaling(lib, scaling, q=A, k=A, v=A, q8=A, k8=A, v8=A, qs=A, ks=A, vs=A, B=1, Hq=2, Hkv=2, N=128,
-                 d=128):
+def prep_ex(lib, scaling, q=A, k=A, v=A, q8=A, k8=A, v8=A, qs=A, ks=A, vs=A, B=1, Hq=2, Hkv=2, N=128, cu=None,
+            d=128):
     P = ctypes.c_void_p
-    return lib.attn_fp8_prepare_scaling(P(q), P(k), P(v), P(q8), P(k8), P(v8), P(qs), P(ks), P(vs),
-                                        B, Hq, Hkv, N, d, None, scaling, None)
+    return lib.attn_fp8_prepare_ex(P(q), P(k), P(v), P(q8), P(k8), P(v8), P(qs), P(ks), P(vs),
+                                   B, Hq, Hkv, N, P(cu) if cu else None, d, None, scaling, None)
 
 
 @pytest.mark.parametrize("scaling,kw,status", [
@@ -114,6 +114,9 @@ def prep_scaling(lib, scaling, q=A, k=A, v=A, q8=A, k8=A, v8=A, qs=A, ks=A, vs=A
     (ea.ATTN_FP8_SCALE_TENSOR, dict(d=256), ea.ATTN_ERR_UNSUPPORTED),
     (ea.ATTN_FP8_SCALE_TENSOR, dict(v8=A + 3), ea.ATTN_ERR_ALIGN),
     (ea.ATTN_FP8_SCALE_BLOCK, dict(B=0), ea.ATTN_ERR_INVALID),
+    (ea.ATTN_FP8_SCALE_BLOCK, dict(cu=A, d=64), ea.ATTN_ERR_UNSUPPORTED),
+    (ea.ATTN_FP8_SCALE_TENSOR, dict(cu=A, k8=A + 8), ea.ATTN_ERR_ALIGN),
+    (ea.ATTN_FP8_SCALE_BLOCK, dict(B=1 << 15, Hq=1 << 10, Hkv=1 << 10, N=1 << 15), ea.ATTN_ERR_UNSUPPORTED),
 ])
-def test_prepare_scaling_validation(lib, scaling, kw, status):
-    assert prep_scaling(lib, scaling, **kw) == status
+def test_prepare_ex_validation(lib, scaling, kw, status):
+    assert prep_ex(lib, scaling, **kw) == status

@@ -6,7 +6,7 @@ Inputs: every element of Q, K and V is N(0,1) + N(0,100) * Bernoulli(0.001), rou
 not give Table 3's).  Reference: the fp64 oracle on the rounded 16-bit values, on sampled rows.
 
 Variants, as in the paper's ablation: FP8 with {one scale per 64-token block, one per tensor}
-x {Hadamard rotation of Q and K, none}, through attn_fp8_prepare / attn_fp8_prepare_scaling and
+x {Hadamard rotation of Q and K, none}, through attn_fp8_prepare / attn_fp8_prepare_ex and
 attn_fwd, plus the bf16 and fp16 paths.  Every FP8 variant must meet the FP8 bar (or the floor
 that quantising its inputs sets, plus 2e-3), and its own error against exact attention on its
 dequantised inputs stays within the kernel's budget; the 16-bit paths meet the 16-bit RMSE and

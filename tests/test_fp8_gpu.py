@@ -5,7 +5,10 @@
   without the Hadamard rotation, for ragged token counts, grouped heads and the full workload;
   the same for attn_fp8_prepare_scaling's per-tensor scales, and for blocks so small that their
   scales sit on the 2^-126 floor, or all zero.
-* attn_fwd on e4m3 inputs against the fp64 oracle run on the *unquantised* bf16 inputs (the
+* the same for packed variable-length sequences (attn_fp8_prepare_ex), blocks restarting at
+  every sequence, with per-block and per-tensor scales.
+* attn_fwd on e4m3 inputs -- dense and packed, causal or not, grouped-query heads -- against
+  the fp64 oracle run on the *unquantised* bf16 inputs (the
   error measure of the FlashAttention-3 digest's section 3.5 / Table 3): O RMSE <= 3e-2, or the
   floor that quantising the inputs sets for any implementation (exact attention on the
   dequantised inputs) plus 2e-3 where that floor is higher.  The kernel's own error (against
@@ -27,22 +30,33 @@ def _dev_bf16(bits):
     return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
 
 
+def _packed(inp):
+    """Keyword arguments selecting the packed layout for a varlen input, else none."""
+    if inp.cu_seqlens is None:
+        return {}
+    return dict(cu_seqlens=torch.from_numpy(inp.cu_seqlens.astype(np.int32)).cuda(), max_seqlen=inp.N)
+
+
 def gpu_prepare(inp, signs, per_tensor=False):
     import exact_attention_76_amd as ea
 
     q, k, v = (_dev_bf16(getattr(inp, n)) for n in "qkv")
     sg = None if signs is None else torch.from_numpy(signs).cuda()
-    out = ea.fp8_prepare(q, k, v, hadamard_signs=sg, per_tensor=per_tensor)
+    out = ea.fp8_prepare(q, k, v, hadamard_signs=sg, per_tensor=per_tensor, **_packed(inp))
     torch.cuda.synchronize()
     return out
 
 
 def oracle_prepare(inp, signs, per_tensor=False):
     q, k, v = (oracle.bf16_to_f64(getattr(inp, n)) for n in "qkv")
+    if inp.cu_seqlens is not None:
+        return ofp8.fp8_prepare_varlen(q, k, v, inp.cu_seqlens, inp.N, signs, per_tensor=per_tensor)
     return ofp8.fp8_prepare(q, k, v, signs, per_tensor=per_tensor)
 
 
 def _assert_prepare_equal(got, want, what):
+    """Codes bit for bit; scales wherever the oracle defines them (packed per-block scales past
+    a sequence's last block are not defined)."""
     names = ["q8", "k8", "v8", "q_scale", "k_scale", "v_scale"]
     for name, g, w in zip(names, got, want):
         g = g.cpu().numpy()
@@ -50,7 +64,8 @@ def _assert_prepare_equal(got, want, what):
             bad = np.argwhere(g != w)
             assert bad.size == 0, f"{what}: {name} differs at {len(bad)} places, first {bad[:3].tolist()}"
         else:
-            assert np.array_equal(g, w.astype(np.float32)), f"{what}: {name} differs"
+            defined = ~np.isnan(w)
+            assert np.array_equal(g[defined], w[defined].astype(np.float32)), f"{what}: {name} differs"
 
 
 @pytest.mark.parametrize("rotate", [True, False])
@@ -113,11 +128,12 @@ def test_prepare_scale_floor_and_zero_blocks(per_tensor, rotate):
                           f"floor/zero prepare per_tensor={per_tensor} rotate={rotate}")
 
 
-def gpu_fp8_attention(inp, signs):
+def gpu_fp8_attention(inp, signs, per_tensor=False):
     import exact_attention_76_amd as ea
 
-    q8, k8, v8, qs, ks, vs = gpu_prepare(inp, signs)
-    o, lse = ea.attention(q8, k8, v8, causal=False, alpha=inp.alpha, q_scale=qs, k_scale=ks, v_scale=vs)
+    q8, k8, v8, qs, ks, vs = gpu_prepare(inp, signs, per_tensor)
+    o, lse = ea.attention(q8, k8, v8, causal=inp.causal, alpha=inp.alpha, q_scale=qs, k_scale=ks, v_scale=vs,
+                          **_packed(inp))
     torch.cuda.synchronize()
     return o.double().cpu().numpy(), lse.double().cpu().numpy(), (q8, k8, v8, qs, ks, vs)
 
@@ -128,10 +144,15 @@ def _three_errors(inp, o, lse, prep, heads, tokens):
     implementation), and kernel vs exact attention on its own dequantised inputs (Z, the
     kernel's own error: P rounded to e4m3 and fp32 arithmetic)."""
     q8, k8, v8, qs, ks, vs = (t.cpu().numpy() for t in prep)
-    qd, kd, vd = ofp8.dequantize(q8, qs), ofp8.dequantize(k8, ks), ofp8.dequantize(v8, vs)
+    cu = inp.cu_seqlens
+    if cu is None:
+        qd, kd, vd = ofp8.dequantize(q8, qs), ofp8.dequantize(k8, ks), ofp8.dequantize(v8, vs)
+    else:
+        qd, kd, vd = (ofp8.dequantize_varlen(c, sc, cu) for c, sc in ((q8, qs), (k8, ks), (v8, vs)))
     q, k, v = gu.widened(inp)
-    o_ref, lse_ref = oracle.attention_rows(q, k, v, heads, tokens, causal=False, alpha=inp.alpha)
-    o_dq, lse_dq = oracle.attention_rows(qd, kd, vd, heads, tokens, causal=False, alpha=inp.alpha)
+    kw = dict(causal=inp.causal, alpha=inp.alpha, cu_seqlens=cu)
+    o_ref, lse_ref = oracle.attention_rows(q, k, v, heads, tokens, **kw)
+    o_dq, lse_dq = oracle.attention_rows(qd, kd, vd, heads, tokens, **kw)
     o_s, lse_s = gu.gpu_rows(inp, o, lse, heads, tokens)
     X = oracle.error_metrics(o_s, o_ref, lse_s, lse_ref)
     Y = oracle.error_metrics(o_dq, o_ref, lse_dq, lse_ref)
@@ -200,3 +221,85 @@ def test_fp8_attention_full_workload_independent_outliers():
     X, Y, Z, lse_dq = _full(inp, 2048)
     check_fp8(X, Y, Z, lse_dq)
     assert X["rmse"] <= gu.TOL_FP8_RMSE, X
+
+
+# ---- packed sequences, causal masks, grouped-query heads ----------------------------------------
+
+VARLEN_SMALL = [1, 63, 64, 65, 200, 129, 300]
+
+
+def _varlen_small(causal, seed):
+    inp = si.varlen_inputs(VARLEN_SMALL, 8, 2, 128, causal=causal, seed=seed)
+    inp.q = si.f32_to_bf16_bits(si.bf16_bits_to_f32(inp.q) * np.float32(3.0))  # several exponents
+    return inp
+
+
+@pytest.mark.parametrize("per_tensor", [False, True])
+@pytest.mark.parametrize("rotate", [True, False])
+def test_prepare_varlen_bit_exact(rotate, per_tensor):
+    inp = _varlen_small(True, 610)
+    signs = si.hadamard_signs(128, seed=55) if rotate else None
+    gu.say("fp8 prepare packed", rotate, per_tensor)
+    _assert_prepare_equal(gpu_prepare(inp, signs, per_tensor), oracle_prepare(inp, signs, per_tensor),
+                          f"packed prepare rotate={rotate} per_tensor={per_tensor}")
+
+
+def _all_rows(inp):
+    T = inp.B * inp.N if inp.cu_seqlens is None else int(inp.cu_seqlens[-1])
+    return np.repeat(np.arange(inp.Hq), T), np.tile(np.arange(T), inp.Hq)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8_attention_dense_gqa(causal):
+    """Ragged N = 300 (three 128-query blocks, the last one partial), 8 query heads on 2 KV
+    heads, every row checked."""
+    inp = si.dense_inputs(2, 300, 8, 128, Hkv=2, causal=causal, seed=611)
+    gu.say("fp8 attention dense GQA", causal)
+    o, lse, prep = gpu_fp8_attention(inp, si.hadamard_signs(128, seed=55))
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    check_fp8(*_three_errors(inp, o, lse, prep, *_all_rows(inp)))
+
+
+@pytest.mark.parametrize("per_tensor", [False, True])
+@pytest.mark.parametrize("causal", [True, False])
+def test_fp8_attention_varlen(causal, per_tensor):
+    """Packed sequences of 1 .. 300 tokens (single-token, one-short, exact and one-over block
+    sizes), GQA 8:2, every row checked."""
+    inp = _varlen_small(causal, 612)
+    gu.say("fp8 attention packed", causal, per_tensor)
+    o, lse, prep = gpu_fp8_attention(inp, si.hadamard_signs(128, seed=55), per_tensor)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    check_fp8(*_three_errors(inp, o, lse, prep, *_all_rows(inp)))
+
+
+def test_fp8_attention_causal_row0_is_v0():
+    """Causal row 0 sees key 0 only, so O_0 is V_0 as quantised (an e4m3 value times a power of
+    two, which bf16 holds exactly): P and l are both 2^8 up to a few fp32 ulps, P rounds to
+    exactly 2^8 in e4m3, and O_0 = V_0 (1 + O(2^-20)) rounds back to V_0.  L_0 is the score of
+    that one key."""
+    inp = si.dense_inputs(1, 256, 4, 128, causal=True, seed=613)
+    gu.say("fp8 causal row 0")
+    o, lse, prep = gpu_fp8_attention(inp, si.hadamard_signs(128, seed=55))
+    q8, k8, v8, qs, ks, vs = (t.cpu().numpy() for t in prep)
+    vd = ofp8.dequantize(v8, vs)[0, 0]  # [H, d]
+    want_o = si.bf16_bits_to_f32(si.f32_to_bf16_bits(vd.astype(np.float32))).astype(np.float64)
+    assert np.array_equal(o[0, 0], want_o)
+    qd, kd = ofp8.dequantize(q8, qs)[0, 0], ofp8.dequantize(k8, ks)[0, 0]
+    s00 = inp.alpha * np.sum(qd * kd, axis=-1)
+    # the one score comes from the matrix core's sum of e4m3 products (see own_lse_bound)
+    assert np.all(np.abs(lse[0, :, 0] - s00) <= np.maximum(gu.TOL_LSE, 2.0 ** -12 * np.abs(s00)))
+
+
+def test_fp8_attention_full_causal():
+    """B=2, H=16, N=8192, d=128, causal, sampled rows."""
+    inp = si.dense_inputs(2, 8192, 16, 128, causal=True, seed=614)
+    gu.say("fp8 attention full causal")
+    check_fp8(*_full(inp, 2048))
+
+
+def test_fp8_attention_full_varlen_gqa():
+    """The packed workload's shape: 8 sequences of 256 .. 8192 tokens, 32 query heads on 8 KV
+    heads, causal, sampled rows (the first and last token of every sequence among them)."""
+    inp = si.CONFIGS["gqa_varlen_causal_hq32_hkv8_d128"]()
+    gu.say("fp8 attention full packed GQA causal")
+    check_fp8(*_full(inp, 2048))
