@@ -49,14 +49,16 @@ PEAK = {"bf16": 2516.6, "fp8": 5033.2}  # dense MFMA TFLOP/s: 256 CU x (4096 | 8
 HBM_PEAK_GBS = 8000.0
 # HBM-side bytes per launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, each scaled by what the
 # same counter reads for a copy kernel of known size (profiles/*_traffic.md).  An entry is valid
-# only for the kernel source it was taken on; any other version reports null.
+# only for the kernel sources it was taken on (sha256 prefix of each file); any other version
+# reports null.
+_DEC = "exact_attention_76_amd/csrc/decompose.h"
 MEASURED_TRAFFIC = {
-    "bf16_mha16k": {"kernel_source": "exact_attention_76_amd/csrc/attn_fwd.hip",
-                    "sha256_prefix": "66af95da9c793b6c", "bytes": 404332430},
-    "fp8_attention": {"kernel_source": "exact_attention_76_amd/csrc/fp8.hip",
-                      "sha256_prefix": "89983e69a3b13bfd", "bytes": 185535377},
-    "fp8_prepare": {"kernel_source": "exact_attention_76_amd/csrc/fp8.hip",
-                    "sha256_prefix": "89983e69a3b13bfd", "bytes": 302667250},
+    "bf16_mha16k": {"sources": {"exact_attention_76_amd/csrc/attn_fwd.hip": "03d0e4e831013a69",
+                                _DEC: "5177b80538cd69cc"}, "bytes": 404032918},
+    "fp8_attention": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "a595a2483b641413",
+                                  _DEC: "5177b80538cd69cc"}, "bytes": 185699483},
+    "fp8_prepare": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "a595a2483b641413"},
+                    "bytes": 302673101},
 }
 
 
@@ -64,12 +66,14 @@ def measured_traffic(key):
     import hashlib
 
     entry = MEASURED_TRAFFIC[key]
-    path = os.path.join(ROOT, entry["kernel_source"])
-    try:
-        digest = hashlib.sha256(open(path, "rb").read()).hexdigest()
-    except OSError:
-        return None
-    return entry["bytes"] if digest.startswith(entry["sha256_prefix"]) else None
+    for rel, prefix in entry["sources"].items():
+        try:
+            digest = hashlib.sha256(open(os.path.join(ROOT, rel), "rb").read()).hexdigest()
+        except OSError:
+            return None
+        if not digest.startswith(prefix):
+            return None
+    return entry["bytes"]
 
 
 def parse():
