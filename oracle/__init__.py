@@ -47,10 +47,10 @@ class OracleLib:
         lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         I64 = ctypes.c_int64
-        lib.oracle_attention_rows.argtypes = [P, P, P, I64, I64, I64, P, I64, ctypes.c_int,
+        lib.oracle_attention_rows.argtypes = [P, P, P, I64, I64, I64, P, I64, ctypes.c_int, I64,
                                               ctypes.c_double, P, P, I64, P, P]
         lib.oracle_attention_rows.restype = ctypes.c_int
-        lib.oracle_attention.argtypes = [P, P, P, I64, I64, I64, P, I64, ctypes.c_int,
+        lib.oracle_attention.argtypes = [P, P, P, I64, I64, I64, P, I64, ctypes.c_int, I64,
                                          ctypes.c_double, P, P]
         lib.oracle_attention.restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
@@ -59,8 +59,9 @@ class OracleLib:
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())
 
-    def attention(self, q, k, v, *, causal: bool = False, alpha: float | None = None, cu_seqlens=None):
-        """fp64 attention over every row.
+    def attention(self, q, k, v, *, causal: bool = False, alpha: float | None = None, cu_seqlens=None,
+                  window: int = 0):
+        """fp64 attention over every row.  ``window`` > 0: query i also needs keys j > i - window.
 
         Dense: q [B,N,Hq,d], k/v [B,N,Hkv,d] -> (o [B,N,Hq,d], lse [B,Hq,N]).
         Varlen: q [T,Hq,d], k/v [T,Hkv,d], cu_seqlens [nseq+1] -> (o [T,Hq,d], lse [Hq,T]).
@@ -75,7 +76,7 @@ class OracleLib:
         o = np.empty((T, Hq, d), dtype=np.float64)
         lse = np.empty((Hq, T), dtype=np.float64)
         rc = self.lib.oracle_attention(_ptr(qp), _ptr(kp), _ptr(vp), Hq, Hkv, d, _ptr(cu), len(cu) - 1,
-                                       int(bool(causal)), alpha, _ptr(o), _ptr(lse))
+                                       int(bool(causal)), int(window), alpha, _ptr(o), _ptr(lse))
         if rc != 0:
             raise ValueError("oracle rejected its arguments")
         if dense:
@@ -84,7 +85,7 @@ class OracleLib:
         return o, lse
 
     def attention_rows(self, q, k, v, heads, tokens, *, causal: bool = False, alpha: float | None = None,
-                       cu_seqlens=None):
+                       cu_seqlens=None, window: int = 0):
         """fp64 attention for selected rows only.
 
         ``tokens`` are packed token indices (dense: b*N + i).  Returns (o [n, d], lse [n]).
@@ -100,7 +101,7 @@ class OracleLib:
         o = np.empty((len(heads), d), dtype=np.float64)
         lse = np.empty(len(heads), dtype=np.float64)
         rc = self.lib.oracle_attention_rows(_ptr(qp), _ptr(kp), _ptr(vp), Hq, Hkv, d, _ptr(cu),
-                                            len(cu) - 1, int(bool(causal)), alpha, _ptr(heads),
+                                            len(cu) - 1, int(bool(causal)), int(window), alpha, _ptr(heads),
                                             _ptr(tokens), len(heads), _ptr(o), _ptr(lse))
         if rc != 0:
             raise ValueError("oracle rejected its arguments")

@@ -22,6 +22,10 @@
  *     FlashAttention-2 style index adjustment the digest mentions in section 3.2 (K and V
  *     are never replicated).
  *   - causal: query i of a sequence sees keys j <= i of the same sequence.
+ *   - sliding window of W keys (window > 0; the guijiagi overview's "sliding window
+ *     attention" paragraph, which only says attention is taken inside a local window):
+ *     query i sees keys j > i - W as well, i.e. with causal the W most recent positions,
+ *     itself included.  window <= 0 means no window.
  *   - a row with no visible key gets O = 0 and L = -inf.
  */
 #include <math.h>
@@ -41,33 +45,35 @@ static int64_t seq_of_token(const int64_t* cu, int64_t nseq, int64_t t) {
 /* One query row (head h, global token t).  o_row receives d values, *lse one value. */
 static void attention_row(const double* q, const double* k, const double* v,
                           int64_t Hq, int64_t Hkv, int64_t d,
-                          const int64_t* cu, int64_t nseq, int causal, double alpha,
+                          const int64_t* cu, int64_t nseq, int causal, int64_t window, double alpha,
                           int64_t h, int64_t t, double* o_row, double* lse) {
   const int64_t b = seq_of_token(cu, nseq, t);
   const int64_t start = cu[b];
   const int64_t n = cu[b + 1] - start;
   const int64_t i = t - start;
   const int64_t g = h / (Hq / Hkv);
-  const int64_t last = causal ? i : n - 1; /* keys start .. start+last are visible */
+  const int64_t last = causal ? i : n - 1; /* keys start+first .. start+last are visible */
+  const int64_t lo = i - window + 1;       /* oldest key inside a window of W keys */
+  const int64_t first = (window > 0 && lo > 0) ? lo : 0;
   const double* qrow = q + (t * Hq + h) * d;
 
   for (int64_t c = 0; c < d; ++c) o_row[c] = 0.0;
-  if (last < 0 || n <= 0) { *lse = -INFINITY; return; }
+  if (last < first || n <= 0) { *lse = -INFINITY; return; }
 
   /* pass 1: scores s_j = alpha * <q, k_j> and their maximum */
-  double* s = (double*)malloc(sizeof(double) * (size_t)(last + 1));
+  double* s = (double*)malloc(sizeof(double) * (size_t)(last - first + 1));
   double m = -INFINITY;
-  for (int64_t j = 0; j <= last; ++j) {
+  for (int64_t j = first; j <= last; ++j) {
     const double* krow = k + ((start + j) * Hkv + g) * d;
     double dot = 0.0;
     for (int64_t c = 0; c < d; ++c) dot += qrow[c] * krow[c];
-    s[j] = alpha * dot;
-    if (s[j] > m) m = s[j];
+    s[j - first] = alpha * dot;
+    if (s[j - first] > m) m = s[j - first];
   }
   /* pass 2: l = sum_j exp(s_j - m), o = sum_j exp(s_j - m) v_j / l */
   double l = 0.0;
-  for (int64_t j = 0; j <= last; ++j) {
-    const double p = exp(s[j] - m);
+  for (int64_t j = first; j <= last; ++j) {
+    const double p = exp(s[j - first] - m);
     const double* vrow = v + ((start + j) * Hkv + g) * d;
     l += p;
     for (int64_t c = 0; c < d; ++c) o_row[c] += p * vrow[c];
@@ -84,7 +90,7 @@ static void attention_row(const double* q, const double* k, const double* v,
  */
 int oracle_attention_rows(const double* q, const double* k, const double* v,
                           int64_t Hq, int64_t Hkv, int64_t d,
-                          const int64_t* cu, int64_t nseq, int causal, double alpha,
+                          const int64_t* cu, int64_t nseq, int causal, int64_t window, double alpha,
                           const int64_t* rows_h, const int64_t* rows_t, int64_t n_rows,
                           double* o, double* lse) {
   if (!q || !k || !v || !cu || !o || !lse || Hq <= 0 || Hkv <= 0 || d <= 0 || nseq <= 0 ||
@@ -95,7 +101,7 @@ int oracle_attention_rows(const double* q, const double* k, const double* v,
     if (rows_h[r] < 0 || rows_h[r] >= Hq || rows_t[r] < 0 || rows_t[r] >= T) return -1;
 #pragma omp parallel for schedule(dynamic, 16)
   for (int64_t r = 0; r < n_rows; ++r)
-    attention_row(q, k, v, Hq, Hkv, d, cu, nseq, causal, alpha, rows_h[r], rows_t[r],
+    attention_row(q, k, v, Hq, Hkv, d, cu, nseq, causal, window, alpha, rows_h[r], rows_t[r],
                   o + r * d, lse + r);
   return 0;
 }
@@ -103,7 +109,7 @@ int oracle_attention_rows(const double* q, const double* k, const double* v,
 /* Every row: o is [T, Hq, d]; lse is [Hq, T]. */
 int oracle_attention(const double* q, const double* k, const double* v,
                      int64_t Hq, int64_t Hkv, int64_t d,
-                     const int64_t* cu, int64_t nseq, int causal, double alpha,
+                     const int64_t* cu, int64_t nseq, int causal, int64_t window, double alpha,
                      double* o, double* lse) {
   if (!q || !k || !v || !cu || !o || !lse || Hq <= 0 || Hkv <= 0 || d <= 0 || nseq <= 0 ||
       Hq % Hkv != 0)
@@ -112,7 +118,7 @@ int oracle_attention(const double* q, const double* k, const double* v,
 #pragma omp parallel for collapse(2) schedule(dynamic, 16)
   for (int64_t t = 0; t < T; ++t)
     for (int64_t h = 0; h < Hq; ++h)
-      attention_row(q, k, v, Hq, Hkv, d, cu, nseq, causal, alpha, h, t,
+      attention_row(q, k, v, Hq, Hkv, d, cu, nseq, causal, window, alpha, h, t,
                     o + (t * Hq + h) * d, lse + h * T + t);
   return 0;
 }

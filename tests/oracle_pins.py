@@ -167,8 +167,9 @@ def pin_golden_weights(lib):
 
 # --- brute force and library cross-checks ------------------------------------------------
 
-def _mp_attention(q, k, v, cu, causal, alpha, Hq, Hkv):
-    """50-digit softmax attention, row by row, straight from the definition."""
+def _mp_attention(q, k, v, cu, causal, alpha, Hq, Hkv, window=0):
+    """50-digit softmax attention, row by row, straight from the definition (window > 0: keys
+    j > t - window only)."""
     mpmath.mp.dps = 50
     T, _, d = q.shape
     o = np.zeros((T, Hq, d))
@@ -180,6 +181,8 @@ def _mp_attention(q, k, v, cu, causal, alpha, Hq, Hkv):
             for h in range(Hq):
                 g = h // (Hq // Hkv)
                 keys = range(st, t + 1) if causal else range(st, en)
+                if window > 0:
+                    keys = [j for j in keys if j > t - window]
                 sc = [a * mpmath.fsum(mpmath.mpf(q[t, h, c]) * mpmath.mpf(k[j, g, c]) for c in range(d))
                       for j in keys]
                 e = [mpmath.exp(x) for x in sc]
@@ -334,6 +337,59 @@ def pin_algorithm1(lib):
             _close(lb, lse[0, 0], 1e-13, f"Alg.1 L Br={Br} Bc={Bc} causal={causal}")
 
 
+# --- sliding window -------------------------------------------------------------------------
+
+def pin_sliding_window(lib):
+    """Causal attention inside a window of W keys (query i sees keys i-W+1 .. i):
+    * Q = 0: O_i is the mean of the last min(W, i+1) V rows and L_i = ln min(W, i+1);
+    * W = 1: O_i = V_i exactly and L_i = s_ii;
+    * W >= N is plain causal attention, bit for bit;
+    * 50-digit brute force on packed sequences with W = 3;
+    * CPU float64 torch scaled_dot_product_attention with the band mask as attn_mask."""
+    B, N, Hq, Hkv, d = 2, 9, 4, 2, 5
+    k, v = _rand((B, N, Hkv, d), 70), _rand((B, N, Hkv, d), 71)
+    q0 = np.zeros((B, N, Hq, d))
+    for W in (1, 3, 4):
+        o, lse = lib.attention(q0, k, v, causal=True, alpha=0.5, window=W)
+        counts = np.minimum(np.arange(1, N + 1), W).astype(np.float64)
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            mean = np.stack([v[:, max(0, i - W + 1):i + 1, g].mean(axis=1) for i in range(N)], axis=1)
+            _close(o[:, :, h], mean, 1e-14, f"window {W} uniform O")
+            _close(lse[:, h], np.log(counts)[None].repeat(B, 0), 1e-14, f"window {W} uniform L")
+    q = _rand((B, N, Hq, d), 72)
+    alpha = 0.4
+    o, lse = lib.attention(q, k, v, causal=True, alpha=alpha, window=1)
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        assert np.array_equal(o[:, :, h], v[:, :, g]), "window 1 is not a copy of V_i"
+        s_ii = alpha * np.einsum("bnd,bnd->bn", q[:, :, h], k[:, :, g])
+        _close(lse[:, h], s_ii, 1e-14, "window 1 L")
+    o_c, lse_c = lib.attention(q, k, v, causal=True, alpha=alpha)
+    for W in (N, N + 5):
+        o_w, lse_w = lib.attention(q, k, v, causal=True, alpha=alpha, window=W)
+        assert np.array_equal(o_w, o_c) and np.array_equal(lse_w, lse_c), f"window {W} >= N is not causal"
+    cu = np.array([0, 2, 7, 13])
+    T = 13
+    qv, kv, vv = _rand((T, 2, 4), 73), _rand((T, 1, 4), 74), _rand((T, 1, 4), 75)
+    o, lse = lib.attention(qv, kv, vv, causal=True, alpha=0.5, cu_seqlens=cu, window=3)
+    o_mp, lse_mp = _mp_attention(qv, kv, vv, cu, True, 0.5, 2, 1, window=3)
+    _close(o, o_mp, 1e-14, "window mpmath O")
+    _close(lse, lse_mp, 1e-14, "window mpmath L")
+    N2, W = 40, 7
+    q, k, v = _rand((1, N2, Hq, 8), 76), _rand((1, N2, Hkv, 8), 77), _rand((1, N2, Hkv, 8), 78)
+    tq = torch.from_numpy(q).permute(0, 2, 1, 3)
+    tk = torch.from_numpy(k).permute(0, 2, 1, 3).repeat_interleave(Hq // Hkv, dim=1)
+    tv = torch.from_numpy(v).permute(0, 2, 1, 3).repeat_interleave(Hq // Hkv, dim=1)
+    i, j = np.arange(N2)[:, None], np.arange(N2)[None, :]
+    band = torch.from_numpy((j <= i) & (j > i - W))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=band, scale=0.3)
+    ref_l = torch.logsumexp((0.3 * (tq @ tk.transpose(-1, -2))).masked_fill(~band, float("-inf")), dim=-1)
+    o, lse = lib.attention(q, k, v, causal=True, alpha=0.3, window=W)
+    _close(o, ref.permute(0, 2, 1, 3).numpy(), 1e-13, "window sdpa O")
+    _close(lse, ref_l.numpy(), 1e-13, "window sdpa L")
+
+
 ALL_PINS = [pin_causal_first_row, pin_uniform_scores, pin_one_hot_key, pin_golden_weights,
             pin_bruteforce_mpmath, pin_torch_sdpa, pin_invariants, pin_rows_match_full,
-            pin_algorithm1]
+            pin_algorithm1, pin_sliding_window]

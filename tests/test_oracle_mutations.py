@@ -15,20 +15,24 @@ from tests import oracle_pins
 SRC = os.path.join(os.path.dirname(oracle.__file__), "attn_oracle.c")
 
 MUTATIONS = {
-    "no_running_max": ("if (s[j] > m) m = s[j];", "(void)m;"),
-    "no_max_subtraction": ("const double p = exp(s[j] - m);", "const double p = exp(s[j]);"),
+    "no_running_max": ("if (s[j - first] > m) m = s[j - first];", "(void)m;"),
+    "no_max_subtraction": ("const double p = exp(s[j - first] - m);", "const double p = exp(s[j - first]);"),
     "gqa_modulo_map": ("const int64_t g = h / (Hq / Hkv);", "const int64_t g = h % Hkv;"),
     "strict_causal": ("const int64_t last = causal ? i : n - 1;", "const int64_t last = causal ? i - 1 : n - 1;"),
     "lse_without_max": ("*lse = m + log(l);", "*lse = log(l);"),
-    "dropped_alpha": ("s[j] = alpha * dot;", "s[j] = dot;"),
+    "dropped_alpha": ("s[j - first] = alpha * dot;", "s[j - first] = dot;"),
     "k_as_value": ("const double* vrow = v + ((start + j) * Hkv + g) * d;",
                    "const double* vrow = k + ((start + j) * Hkv + g) * d;"),
     "no_normalisation": ("for (int64_t c = 0; c < d; ++c) o_row[c] /= l;", ""),
-    "dropped_last_key": ("for (int64_t j = 0; j <= last; ++j) {\n    const double p",
-                         "for (int64_t j = 0; j < last; ++j) {\n    const double p"),
+    "dropped_last_key": ("for (int64_t j = first; j <= last; ++j) {\n    const double p",
+                         "for (int64_t j = first; j < last; ++j) {\n    const double p"),
     "query_from_key_head": ("const double* qrow = q + (t * Hq + h) * d;",
                             "const double* qrow = q + (t * Hq + g) * d;"),
     "sequence_end_ignored": ("const int64_t n = cu[b + 1] - start;", "const int64_t n = cu[nseq] - start;"),
+    "window_off_by_one": ("const int64_t lo = i - window + 1;", "const int64_t lo = i - window;"),
+    "window_ignored": ("const int64_t first = (window > 0 && lo > 0) ? lo : 0;", "const int64_t first = 0;"),
+    "window_from_sequence_start": ("const int64_t first = (window > 0 && lo > 0) ? lo : 0;",
+                                   "const int64_t first = (window > 0 && lo > 0) ? lo - (int64_t)(start > 0) : 0;"),
 }
 
 
