@@ -14,6 +14,8 @@ sweep's aggregate (total FLOPs over total time).  ``--workload`` selects the oth
           (Hadamard rotation + block quantisation, HBM-bound) is timed separately
   fp8_causal  the same kernel causal, on the bf16 causal d=128 workload's inputs
   fp8_varlen  the same kernel on the packed causal GQA workload's inputs
+  window  causal sliding window of 4096 keys, B=1 N=16384 H=16 d=128 (the headline's inputs), bf16
+          then e4m3; FLOPs count the visible pairs, n^2/2 - (n-W)^2/2 per head
   ceiling the matrix-core ceiling the attention kernels run against: back-to-back
           v_mfma_f32_32x32x16_bf16 on random operands on every CU (2 and 4 waves per SIMD),
           with no LDS or vector-ALU work; under the chip's power limit this sits well below
@@ -53,11 +55,11 @@ HBM_PEAK_GBS = 8000.0
 # reports null.
 _DEC = "exact_attention_76_amd/csrc/decompose.h"
 MEASURED_TRAFFIC = {
-    "bf16_mha16k": {"sources": {"exact_attention_76_amd/csrc/attn_fwd.hip": "03d0e4e831013a69",
+    "bf16_mha16k": {"sources": {"exact_attention_76_amd/csrc/attn_fwd.hip": "9db5dce1e60553b2",
                                 _DEC: "5177b80538cd69cc"}, "bytes": 404032918},
-    "fp8_attention": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "a595a2483b641413",
+    "fp8_attention": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "c53af65c5945ed85",
                                   _DEC: "5177b80538cd69cc"}, "bytes": 185699483},
-    "fp8_prepare": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "a595a2483b641413"},
+    "fp8_prepare": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "c53af65c5945ed85"},
                     "bytes": 302673101},
 }
 
@@ -82,7 +84,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mha16k", choices=["mha16k", "sweep", "causal", "varlen", "fp8", "fp8_causal",
-                                                              "fp8_varlen", "ceiling"])
+                                                              "fp8_varlen", "window", "ceiling"])
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -177,6 +179,8 @@ def line(args, name, inp, flops, ms_wall, ms_gpu, dtype, extra=None, traffic=Non
     cfg = {"workload": name, "B": inp.B, "N": inp.N, "Hq": inp.Hq, "Hkv": inp.Hkv, "d": inp.d,
            "causal": inp.causal, "varlen": inp.cu_seqlens is not None, "tokens": inp.total_tokens,
            "flops_per_step": flops, "pct_of_peak": round(100 * tflops / peak, 2), "parallelism": "single GPU"}
+    if inp.window:
+        cfg["window"] = inp.window
     if launches is not None:
         med, best = launches
         cfg.update({"ms_event_mean": round(ms_gpu, 4), "ms_launch_median": round(med, 4), "ms_launch_min": round(best, 4),
@@ -209,8 +213,12 @@ def run_16bit(args, name, inp, dev, stream, traffic=None, cpu=False):
         cu = torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(dev)
 
     def step():
-        ea.attn_fwd(q, k, v, o, lse, causal=inp.causal, alpha=inp.alpha, cu_seqlens=cu,
-                    max_seqlen=inp.N if cu is not None else None, stream=stream)
+        if inp.window:
+            ea.attn_fwd_window(q, k, v, o, lse, window=inp.window, alpha=inp.alpha, cu_seqlens=cu,
+                               max_seqlen=inp.N if cu is not None else None, stream=stream)
+        else:
+            ea.attn_fwd(q, k, v, o, lse, causal=inp.causal, alpha=inp.alpha, cu_seqlens=cu,
+                        max_seqlen=inp.N if cu is not None else None, stream=stream)
 
     ms_wall, ms_gpu = timed(step, stream, args.steps, args.warmup)
     launches = per_launch(step, stream, args.steps)
@@ -222,16 +230,25 @@ def run_16bit(args, name, inp, dev, stream, traffic=None, cpu=False):
 # FP8 workloads: name of the line -> the seeded bf16 inputs it quantises
 FP8_WORKLOADS = {"fp8": "fp8_b2_h16_n8192_d128", "fp8_causal": "causal_b2_h16_n8192_d128",
                  "fp8_varlen": "gqa_varlen_causal_hq32_hkv8_d128"}
+WINDOW = 4096  # keys of the sliding-window workload
 
 
-def run_fp8(args, dev, stream, workload="fp8"):
+def window_inputs():
+    import seeded_inputs as si
+
+    inp = si.CONFIGS["mha_n16384_b1_h16_d128"]()
+    inp.causal, inp.window = True, WINDOW
+    return inp
+
+
+def run_fp8(args, dev, stream, workload="fp8", inp=None):
     import torch
 
     import exact_attention_76_amd as ea
     import seeded_inputs as si
 
-    src = FP8_WORKLOADS[workload]
-    inp = si.CONFIGS[src]()
+    src = FP8_WORKLOADS.get(workload, workload)
+    inp = si.CONFIGS[src]() if inp is None else inp
     q, k, v = (to_dev(getattr(inp, n), "bf16", dev) for n in "qkv")
     signs = torch.from_numpy(si.hadamard_signs(inp.d)).to(dev)
     packed = {}
@@ -243,8 +260,11 @@ def run_fp8(args, dev, stream, workload="fp8"):
     lse = torch.empty(lse_shape, dtype=torch.float32, device=dev)
 
     def attn():
-        ea.attn_fwd(q8, k8, v8, o, lse, causal=inp.causal, alpha=inp.alpha, q_scale=qs, k_scale=ks, v_scale=vs,
-                    stream=stream, **packed)
+        kw = dict(alpha=inp.alpha, q_scale=qs, k_scale=ks, v_scale=vs, stream=stream, **packed)
+        if inp.window:
+            ea.attn_fwd_window(q8, k8, v8, o, lse, window=inp.window, **kw)
+        else:
+            ea.attn_fwd(q8, k8, v8, o, lse, causal=inp.causal, **kw)
 
     def prep():
         ea.attn_fp8_prepare_ex(q, k, v, q8, k8, v8, qs, ks, vs, hadamard_signs=signs, stream=stream, **packed)
@@ -263,6 +283,8 @@ def run_fp8(args, dev, stream, workload="fp8"):
                                   "bytes_per_launch": prep_bytes},
              "prepare_plus_attention_tflops": round(inp.flops() / ((pw + ms_wall) * 1e-3) / 1e12, 2)}
     name = "fp8_b2_h16_n8192_d128" if workload == "fp8" else f"fp8_{src}"
+    if inp.window:
+        name = f"fp8_window{inp.window}_b1_h16_n16384_d128"
     return line(args, name, inp, inp.flops(), ms_wall, ms_gpu, "fp8", extra=extra,
                 traffic=measured_traffic("fp8_attention") if workload == "fp8" else None, launches=launches)
 
@@ -361,6 +383,9 @@ def main():
             out = [run_16bit(args, n, si.CONFIGS[n](), dev, stream)]
         elif args.workload in FP8_WORKLOADS:
             out = [run_fp8(args, dev, stream, args.workload)]
+        elif args.workload == "window":
+            out = [run_16bit(args, f"window{WINDOW}_b1_h16_n16384_d128", window_inputs(), dev, stream),
+                   run_fp8(args, dev, stream, "mha_n16384_b1_h16_d128", inp=window_inputs())]
         else:
             out = run_ceiling(args, dev, stream)
     for o in out:

@@ -8,6 +8,7 @@ Entry points carry the names of the C ABI:
 
 * :func:`attn_fwd` -- O and LSE of exact attention (bf16 / fp16 / fp8-e4m3 inputs; dense or
   packed variable-length; causal or not; grouped-query heads).
+* :func:`attn_fwd_window` -- the same, causal, inside a sliding window of W keys.
 * :func:`attn_fp8_prepare` -- Hadamard rotation + per-block power-of-two e4m3 quantisation.
 * :func:`attn_fp8_prepare_ex` -- the same for packed sequences too, with per-block or per-tensor
   scales.
@@ -23,7 +24,7 @@ import re
 
 import torch
 
-__all__ = ["AttnError", "attn_fwd", "attn_fp8_prepare", "attn_fp8_prepare_ex", "attn_strerror", "attention",
+__all__ = ["AttnError", "attn_fwd", "attn_fwd_window", "attn_fp8_prepare", "attn_fp8_prepare_ex", "attn_strerror", "attention",
            "fp8_prepare", "load_library", "LIB_PATH", "ATTN_BF16", "ATTN_FP16", "ATTN_FP8_E4M3",
            "ATTN_FP8_SCALE_BLOCK", "ATTN_FP8_SCALE_TENSOR"]
 
@@ -59,6 +60,8 @@ def load_library(build_if_missing: bool = True):
     P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, P, I, I, F, I, P, P, P, P]
     lib.attn_fwd.restype = I
+    lib.attn_fwd_window.argtypes = [P, P, P, P, P, I, I, I, I, P, I, I, F, I, P, P, P, P]
+    lib.attn_fwd_window.restype = I
     lib.attn_fp8_prepare.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, P]
     lib.attn_fp8_prepare.restype = I
     lib.attn_fp8_prepare_ex.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, P, I, P, I, P]
@@ -124,15 +127,8 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported input dtype {t.dtype}")
 
 
-def attn_fwd(q, k, v, o, lse, *, causal: bool = False, alpha: float | None = None, cu_seqlens=None,
-             max_seqlen: int | None = None, q_scale=None, k_scale=None, v_scale=None, stream=None) -> None:
-    """Enqueue attn_fwd on ``stream`` (default: torch's current stream).
-
-    Dense: q/o [B, N, Hq, d], k/v [B, N, Hkv, d], lse [B, Hq, N].
-    Varlen: q/o [T, Hq, d], k/v [T, Hkv, d], lse [Hq, T], cu_seqlens int32 [B+1] on the GPU and
-    ``max_seqlen`` >= the longest sequence.  fp8 inputs (float8_e4m3fn or uint8 codes) need the
-    three per-block scale tensors.
-    """
+def _fwd_call(q, k, v, o, lse, cu_seqlens, max_seqlen, q_scale, k_scale, v_scale, alpha):
+    """Check the attn_fwd tensors; return the device and the C arguments around the mode."""
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse)):
         _check_tensor(t, name)
     if lse.dtype != torch.float32:
@@ -177,18 +173,45 @@ def attn_fwd(q, k, v, o, lse, *, causal: bool = False, alpha: float | None = Non
     alpha = (1.0 / d ** 0.5) if alpha is None else float(alpha)
     dev = _one_device((("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("cu_seqlens", cu_seqlens),
                        ("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)))
+    head = (_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, _ptr(cu_seqlens), d)
+    tail = (alpha, dt, _ptr(q_scale), _ptr(k_scale), _ptr(v_scale))
+    return dev, head, tail
+
+
+def attn_fwd(q, k, v, o, lse, *, causal: bool = False, alpha: float | None = None, cu_seqlens=None,
+             max_seqlen: int | None = None, q_scale=None, k_scale=None, v_scale=None, stream=None) -> None:
+    """Enqueue attn_fwd on ``stream`` (default: torch's current stream).
+
+    Dense: q/o [B, N, Hq, d], k/v [B, N, Hkv, d], lse [B, Hq, N].
+    Varlen: q/o [T, Hq, d], k/v [T, Hkv, d], lse [Hq, T], cu_seqlens int32 [B+1] on the GPU and
+    ``max_seqlen`` >= the longest sequence.  fp8 inputs (float8_e4m3fn or uint8 codes) need the
+    three per-block scale tensors.
+    """
+    dev, head, tail = _fwd_call(q, k, v, o, lse, cu_seqlens, max_seqlen, q_scale, k_scale, v_scale, alpha)
     lib = load_library()
     with torch.cuda.device(dev):
-        st = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, N, _ptr(cu_seqlens), d,
-                          int(bool(causal)), alpha, dt, _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
-                          _stream_handle(stream, dev))
+        st = lib.attn_fwd(*head, int(bool(causal)), *tail, _stream_handle(stream, dev))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd")
 
 
+def attn_fwd_window(q, k, v, o, lse, *, window: int, alpha: float | None = None, cu_seqlens=None,
+                    max_seqlen: int | None = None, q_scale=None, k_scale=None, v_scale=None, stream=None) -> None:
+    """Enqueue attn_fwd_window: causal attention in which query i sees keys i-window+1 .. i.
+    Tensors as for :func:`attn_fwd`."""
+    dev, head, tail = _fwd_call(q, k, v, o, lse, cu_seqlens, max_seqlen, q_scale, k_scale, v_scale, alpha)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        st = lib.attn_fwd_window(*head, int(window), *tail, _stream_handle(stream, dev))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_fwd_window")
+
+
 def attention(q, k, v, *, causal: bool = False, alpha: float | None = None, cu_seqlens=None,
-              max_seqlen: int | None = None, q_scale=None, k_scale=None, v_scale=None, stream=None):
-    """Allocate O (bf16, or fp16 for fp16 inputs) and LSE (fp32) and call :func:`attn_fwd`."""
+              max_seqlen: int | None = None, q_scale=None, k_scale=None, v_scale=None, window: int | None = None,
+              stream=None):
+    """Allocate O (bf16, or fp16 for fp16 inputs) and LSE (fp32) and call :func:`attn_fwd`, or,
+    with ``window``, :func:`attn_fwd_window` (causal sliding window; ``causal`` is then implied)."""
     out_dtype = torch.float16 if q.dtype == torch.float16 else torch.bfloat16
     o = torch.empty(q.shape, dtype=out_dtype, device=q.device)
     if cu_seqlens is None:
@@ -197,8 +220,12 @@ def attention(q, k, v, *, causal: bool = False, alpha: float | None = None, cu_s
     else:
         T, Hq, _ = q.shape
         lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
-    attn_fwd(q, k, v, o, lse, causal=causal, alpha=alpha, cu_seqlens=cu_seqlens, max_seqlen=max_seqlen,
-             q_scale=q_scale, k_scale=k_scale, v_scale=v_scale, stream=stream)
+    kw = dict(alpha=alpha, cu_seqlens=cu_seqlens, max_seqlen=max_seqlen, q_scale=q_scale, k_scale=k_scale,
+              v_scale=v_scale, stream=stream)
+    if window is not None:
+        attn_fwd_window(q, k, v, o, lse, window=window, **kw)
+    else:
+        attn_fwd(q, k, v, o, lse, causal=causal, **kw)
     return o, lse
 
 

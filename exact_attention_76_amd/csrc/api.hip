@@ -30,32 +30,17 @@ int status_of(hipError_t err) {
   return ATTN_ERR_HIP;
 }
 
-}  // namespace
-
-extern "C" {
-
-const char* attn_strerror(int status) {
-  switch (status) {
-    case ATTN_OK: return "success";
-    case ATTN_ERR_INVALID: return "invalid argument (null pointer, non-positive size, Hq % Hkv != 0, "
-                                  "alpha not finite and > 0, or FP8 without scales)";
-    case ATTN_ERR_UNSUPPORTED: return "unsupported combination of head dim, dtype and mode";
-    case ATTN_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
-    case ATTN_ERR_HIP: return "HIP runtime refused the launch";
-    default: return "unknown status";
-  }
-}
-
-int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
-             int N, const int* cu_seqlens, int d, int causal, float alpha, attn_dtype_t dtype,
-             const float* q_scale, const float* k_scale, const float* v_scale, hipStream_t stream) {
+// attn_fwd and attn_fwd_window: window = 0 is no window.
+int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int N,
+        const int* cu_seqlens, int d, int causal, int window, float alpha, attn_dtype_t dtype, const float* q_scale,
+        const float* k_scale, const float* v_scale, hipStream_t stream) {
   int rc = validate_common(q, k, v, o, lse, B, Hq, Hkv, N);
   if (rc != ATTN_OK) return rc;
   if (!(isfinite(alpha) && alpha > 0.f)) return ATTN_ERR_INVALID;
   if (causal != 0 && causal != 1) return ATTN_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return ATTN_ERR_ALIGN;
 
-  attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, cu_seqlens, d, causal, alpha, q_scale, k_scale, v_scale};
+  attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, N, cu_seqlens, d, causal, window, alpha, q_scale, k_scale, v_scale};
   hipError_t err;
   switch (dtype) {
     case ATTN_BF16:
@@ -75,6 +60,38 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
       return ATTN_ERR_UNSUPPORTED;
   }
   return status_of(err);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_strerror(int status) {
+  switch (status) {
+    case ATTN_OK: return "success";
+    case ATTN_ERR_INVALID: return "invalid argument (null pointer, non-positive size, Hq % Hkv != 0, "
+                                  "alpha not finite and > 0, or FP8 without scales)";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported combination of head dim, dtype and mode";
+    case ATTN_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
+    case ATTN_ERR_HIP: return "HIP runtime refused the launch";
+    default: return "unknown status";
+  }
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+             int N, const int* cu_seqlens, int d, int causal, float alpha, attn_dtype_t dtype,
+             const float* q_scale, const float* k_scale, const float* v_scale, hipStream_t stream) {
+  return fwd(q, k, v, o, lse, B, Hq, Hkv, N, cu_seqlens, d, causal, 0, alpha, dtype, q_scale, k_scale, v_scale,
+             stream);
+}
+
+int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                    int N, const int* cu_seqlens, int d, int window, float alpha, attn_dtype_t dtype,
+                    const float* q_scale, const float* k_scale, const float* v_scale, hipStream_t stream) {
+  if (window < 1) return ATTN_ERR_INVALID;
+  // a window of N or more keys is plain causal attention
+  return fwd(q, k, v, o, lse, B, Hq, Hkv, N, cu_seqlens, d, 1, window < N ? window : 0, alpha, dtype, q_scale,
+             k_scale, v_scale, stream);
 }
 
 int attn_fp8_prepare(const void* q, const void* k, const void* v, void* q8, void* k8, void* v8,

@@ -160,11 +160,12 @@ struct LoopShape {
 // (no LDS access moves across it); LDS reads of this wave are complete before it arrives.
 __device__ __forceinline__ void phase_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-template <int D, int BC, typename SH, bool BF16, bool CAUSAL, bool VARLEN>
+// WINDOW (implies CAUSAL): causal sliding window of `window` keys; otherwise `window` is unused.
+template <int D, int BC, typename SH, bool BF16, bool CAUSAL, bool VARLEN, bool WINDOW>
 __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int N,
-    const int* __restrict__ cu_seqlens, int nseq, float alpha, int num_qblocks) {
+    const int* __restrict__ cu_seqlens, int nseq, float alpha, int num_qblocks, int window) {
   constexpr int WAVES = SH::WAVES;
   constexpr int BR = 32 * WAVES;                   // queries per workgroup
   constexpr int NCH = D / 8;                       // 16-byte chunks per row
@@ -266,8 +267,17 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
   float l = 0.f;        // running sum over this lane's keys (lane halves are added at the end)
   const float c = alpha * kLog2e;
 
+  static_assert(!WINDOW || CAUSAL, "a sliding window is causal");
   const int kv_end = CAUSAL ? min(n, q0 + BR) : n;
-  const int ntiles = (kv_end + BC - 1) / BC;
+  // Sliding window: query i sees keys i-window+1 .. i.  Tiles before t0 hold no key any query
+  // of the workgroup sees; the loops count tiles from t0.
+  const int t0 = WINDOW ? max(0, q0 - window + 1) / BC : 0;
+  const int ntiles = (kv_end + BC - 1) / BC - t0;
+  // whether this wave sees any key of loop tile j (it still copies and passes the barriers)
+  auto wave_needs = [&](int j) {
+    const int k0 = (t0 + j) * BC;
+    return !CAUSAL || (k0 <= qw + 31 && (!WINDOW || k0 + BC - 1 > qw - window));
+  };
 
   // S^T = K Q^T: lane holds query qi, keys k0 + 32*cb + 8*(r/4) + 4*hi + r%4
   auto gemm1 = [&](const char* ks, f32x16* s) {
@@ -281,17 +291,22 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
       }
     }
   };
-  // Mask, running maximum and lazy rescale of tile j; returns the stabiliser m*c.
+  // Mask, running maximum and lazy rescale of loop tile j; returns the stabiliser m*c.  A lane
+  // whose keys in the tile are all masked keeps m = -inf and adds nothing.
   auto update_max = [&](f32x16* s, int j) -> float {
-    const int k0 = j * BC;
-    const bool need_mask = (k0 + BC > n) || (CAUSAL && k0 + BC - 1 > qw);
+    const int k0 = (t0 + j) * BC;
+    const bool need_mask = (k0 + BC > n) || (CAUSAL && (k0 + BC - 1 > qw || (WINDOW && k0 <= qw + 31 - window)));
     if (need_mask) {
 #pragma unroll
       for (int cb = 0; cb < NB_C; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + cb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (key >= n || (CAUSAL && key > qi)) s[cb][r] = -INFINITY;
+          if constexpr (WINDOW) {  // visible iff 0 <= qi - key < window (one unsigned compare)
+            if (key >= n || (unsigned)(qi - key) >= (unsigned)window) s[cb][r] = -INFINITY;
+          } else {
+            if (key >= n || (CAUSAL && key > qi)) s[cb][r] = -INFINITY;
+          }
         }
     }
     float mt = -INFINITY;
@@ -361,17 +376,17 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
 
   if constexpr (!SH::PP) {
     // ---- main loop: two buffer pairs, unrolled by two so each half names its buffers ----
-    issue_tile(kb0, vb0, 0);
-    __builtin_amdgcn_s_waitcnt(0);  // Q fragments and tile 0 have arrived
+    issue_tile(kb0, vb0, t0);
+    __builtin_amdgcn_s_waitcnt(0);  // Q fragments and the first tile have arrived
     __syncthreads();
     for (int j = 0; j < ntiles; j += 2) {
-      if (j + 1 < ntiles) issue_tile(kb1, vb1, j + 1);
-      if (!CAUSAL || j * BC <= qw + 31) compute_tile(kb0, vb0, j);
+      if (j + 1 < ntiles) issue_tile(kb1, vb1, t0 + j + 1);
+      if (wave_needs(j)) compute_tile(kb0, vb0, j);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (j + 1 >= ntiles) break;
-      if (j + 2 < ntiles) issue_tile(kb0, vb0, j + 2);
-      if (!CAUSAL || (j + 1) * BC <= qw + 31) compute_tile(kb1, vb1, j + 1);
+      if (j + 2 < ntiles) issue_tile(kb0, vb0, t0 + j + 2);
+      if (wave_needs(j + 1)) compute_tile(kb1, vb1, j + 1);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
@@ -399,13 +414,16 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
       tile_row_chunk<D>(wb * NIB * 64 + lane, row, chunk);
       voffb = row * rowbytes + chunk * 16;
     }
-    // copies of this wave's part of one tile; a tile past the end reads as zero
-    auto copy = [&](const char* base, char* dst, int tile) {
-      const int64_t off = (int64_t)tile * BC * rowbytes;
+    // copies of this wave's part of loop tile j; a tile past the end reads as zero
+    auto copy = [&](const char* base, char* dst, int j) {
+      const int64_t off = (int64_t)(t0 + j) * BC * rowbytes;
       const int rem = off < nbytes ? (int)(nbytes - off) : 0;
       copy_rows_to_lds<NIB, IPB>(base + (rem ? off : 0), rem, dst + wb * NIB * 1024, voffb, blk_bytes);
     };
-    const int jw = CAUSAL ? min(ntiles, (qw + 31) / BC + 1) : ntiles;  // tiles this wave needs
+    // loop tiles jlo .. jw-1 hold keys this wave sees (causal: up to its diagonal, and from its
+    // first query's window on)
+    const int jw = CAUSAL ? min(ntiles, (qw + 31) / BC + 1 - t0) : ntiles;
+    const int jlo = WINDOW ? max(0, qw - window + 1) / BC - t0 : 0;
     f32x16 s[NB_C];
     u32x4 pf[KS_C];
     // An M phase is one stream of products (the second product of the previous tile, then the
@@ -433,11 +451,11 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
         s[cb] = mma32<BF16>(a, qf[st], s[cb]);
       }
     };
-    // Every M phase up to this wave's last tile runs the whole stream: in M_0 P is zero and
-    // the V buffer holds a copy of V_0 (finite values), so the second product adds exact
-    // zeros; in M_jw the first product is formed and not used.
+    // Every M phase from this wave's first tile to its last runs the whole stream: in M_jlo P is
+    // still zero and the V buffer holds finite values (in M_0 a copy of V_0), so the second
+    // product adds exact zeros; in M_jw the first product is formed and not used.
     auto mphase = [&](const char* ks, const char* vs, int j) {
-      if (j <= jw) {
+      if (j >= jlo && j <= jw) {
         u32x4 win[PD];
 #pragma unroll
         for (int i = 0; i < PD; ++i) win[i] = operand(ks, vs, i);
@@ -468,7 +486,7 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
     auto vphase = [&](char* kdst, char* vdst, int j) {
       if (!second) copy(kbase, kdst, j + 2);
       else copy(vbase, vdst, j + 1);
-      if (j < jw) {
+      if (j >= jlo && j < jw) {
         const float mc = update_max(s, j);
         float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
@@ -545,16 +563,16 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
   }
 }
 
-template <int D, int BC, typename SH, bool BF16, bool CAUSAL, bool VARLEN>
+template <int D, int BC, typename SH, bool BF16, bool CAUSAL, bool VARLEN, bool WINDOW = false>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   constexpr int BR = 32 * SH::WAVES;
   const int nqb = (a.N + BR - 1) / BR;
   const long long grid = (long long)nqb * a.Hq * a.B;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_kernel<D, BC, SH, BF16, CAUSAL, VARLEN>), dim3((unsigned)grid), dim3(64 * SH::WAVES), 0,
+  hipLaunchKernelGGL((fwd_kernel<D, BC, SH, BF16, CAUSAL, VARLEN, WINDOW>), dim3((unsigned)grid), dim3(64 * SH::WAVES), 0,
                      stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, a.Hq, a.Hkv,
-                     a.N, a.cu_seqlens, a.B, a.alpha, nqb);
+                     a.N, a.cu_seqlens, a.B, a.alpha, nqb, a.window);
   return hipGetLastError();
 }
 
@@ -566,11 +584,18 @@ hipError_t launch_modes(const FwdArgs& a, hipStream_t stream) {
   return varlen ? launch<D, BC, SH, BF16, false, true>(a, stream) : launch<D, BC, SH, BF16, false, false>(a, stream);
 }
 
+template <int D, int BC, typename SH, bool BF16>
+hipError_t launch_window(const FwdArgs& a, hipStream_t stream) {
+  return a.cu_seqlens != nullptr ? launch<D, BC, SH, BF16, true, true, true>(a, stream)
+                                 : launch<D, BC, SH, BF16, true, false, true>(a, stream);
+}
+
 // Per head dim: keys per tile and loop shape.  Eight waves (256 queries) per workgroup, one
 // workgroup per CU: the K/V tile copies are shared by all eight waves.  d = 128 and d = 256 run
 // the ping-pong loop (measured on MI355X: +4-7% over the plain loop); at d = 64 the softmax
 // outweighs the products and the plain loop, which lets the two waves of a SIMD share the
-// VALU freely, is as fast.
+// VALU freely, is as fast.  With a sliding window, d = 256 runs the plain loop: the window's
+// bookkeeping does not fit the ping-pong loop's 256 registers without spilling.
 #ifndef ATTN_D64_SHAPE
 #define ATTN_D64_SHAPE 64, LoopShape<8, false>
 #endif
@@ -580,9 +605,20 @@ hipError_t launch_modes(const FwdArgs& a, hipStream_t stream) {
 #ifndef ATTN_D256_SHAPE
 #define ATTN_D256_SHAPE 32, LoopShape<8, false, true, 4>
 #endif
+#ifndef ATTN_D256_WINDOW_SHAPE
+#define ATTN_D256_WINDOW_SHAPE 32, LoopShape<8, false>
+#endif
 
 template <bool BF16>
 hipError_t launch_dims(const FwdArgs& a, hipStream_t stream) {
+  if (a.window > 0) {
+    switch (a.d) {
+      case 64: return launch_window<64, ATTN_D64_SHAPE, BF16>(a, stream);
+      case 128: return launch_window<128, ATTN_D128_SHAPE, BF16>(a, stream);
+      case 256: return launch_window<256, ATTN_D256_WINDOW_SHAPE, BF16>(a, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (a.d) {
     case 64: return launch_modes<64, ATTN_D64_SHAPE, BF16>(a, stream);
     case 128: return launch_modes<128, ATTN_D128_SHAPE, BF16>(a, stream);

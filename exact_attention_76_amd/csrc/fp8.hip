@@ -285,12 +285,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // WAVES waves of 32 queries per workgroup; BC keys per tile (64 or 128, a multiple of the
 // 64-token scale block).  CAUSAL: key j visible to query i iff j <= i.  VARLEN: packed sequences
 // [T, H, d] delimited by cu_seqlens, scale blocks counted from each sequence's first token.
-template <int WAVES, int BC, bool CAUSAL, bool VARLEN>
+// WINDOW (implies CAUSAL): query i sees keys i-window+1 .. i only.
+template <int WAVES, int BC, bool CAUSAL, bool VARLEN, bool WINDOW>
 __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 3 : 1)) void fwd_fp8_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
     const float* __restrict__ qs, const float* __restrict__ ks_, const float* __restrict__ vs_,
     uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int N, const int* __restrict__ cu_seqlens,
-    int nseq, float alpha, int num_qblocks) {
+    int nseq, float alpha, int num_qblocks, int window) {
   constexpr int BR = 32 * WAVES;        // queries per workgroup
   constexpr int TILE = BC * kD;         // bytes of one K or V tile
   constexpr int NI = TILE / 1024 / WAVES;  // 1 KB copies per wave per tensor
@@ -376,12 +377,19 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 3 : 1)) void fwd_fp8_kern
   float l = 0.f;
   const float c = alpha * kLog2e;
   const int kv_end = CAUSAL ? min(n, q0 + BR) : n;  // keys any query of the workgroup sees
-  const int ntiles = (kv_end + BC - 1) / BC;
+  static_assert(!WINDOW || CAUSAL, "a sliding window is causal");
+  // the loop counts tiles from t0, the first one any query of the workgroup sees
+  const int t0 = WINDOW ? max(0, q0 - window + 1) / BC : 0;
+  const int ntiles = (kv_end + BC - 1) / BC - t0;
+  auto wave_needs = [&](int j) {  // this wave sees a key of loop tile j
+    const int k0 = (t0 + j) * BC;
+    return !CAUSAL || (k0 <= qw + 31 && (!WINDOW || k0 + BC - 1 > qw - window));
+  };
 
   auto compute_tile = [&](const char* stage, int j) {
     const char* kt = stage;
     const char* vt = stage + TILE;
-    const int k0 = j * BC;
+    const int k0 = (t0 + j) * BC;
     f32x16 s[NB_C];
 #pragma unroll
     for (int cb = 0; cb < NB_C; ++cb) {
@@ -395,13 +403,17 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 3 : 1)) void fwd_fp8_kern
         s[cb] = mma_f8(a, qf[st], s[cb], sk, sq);
       }
     }
-    if (k0 + BC > n || (CAUSAL && k0 + BC - 1 > qw)) {
+    if (k0 + BC > n || (CAUSAL && (k0 + BC - 1 > qw || (WINDOW && k0 <= qw + 31 - window)))) {
 #pragma unroll
       for (int cb = 0; cb < NB_C; ++cb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + cb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
-          if (key >= n || (CAUSAL && key > qi)) s[cb][r] = -INFINITY;
+          if constexpr (WINDOW) {  // visible iff 0 <= qi - key < window (one unsigned compare)
+            if (key >= n || (unsigned)(qi - key) >= (unsigned)window) s[cb][r] = -INFINITY;
+          } else {
+            if (key >= n || (CAUSAL && key > qi)) s[cb][r] = -INFINITY;
+          }
         }
     }
     float mt = -INFINITY;
@@ -461,19 +473,20 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 3 : 1)) void fwd_fp8_kern
     }
   };
 
-  issue_tile(st0, 0);
+  issue_tile(st0, t0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  // causal: a wave skips the tiles that lie wholly above its diagonal (its first tile always has
-  // visible keys, so its running maximum is finite from then on); it still copies and waits
+  // causal: a wave skips the tiles that lie wholly above its diagonal or before its window; it
+  // still copies and waits.  A lane whose keys in a tile are all masked keeps m = -inf and adds
+  // nothing (P = exp2(-inf) = 0).
   for (int j = 0; j < ntiles; j += 2) {
-    if (j + 1 < ntiles) issue_tile(st1, j + 1);
-    if (!CAUSAL || j * BC <= qw + 31) compute_tile(st0, j);
+    if (j + 1 < ntiles) issue_tile(st1, t0 + j + 1);
+    if (wave_needs(j)) compute_tile(st0, j);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (j + 1 >= ntiles) break;
-    if (j + 2 < ntiles) issue_tile(st0, j + 2);
-    if (!CAUSAL || (j + 1) * BC <= qw + 31) compute_tile(st1, j + 1);
+    if (j + 2 < ntiles) issue_tile(st0, t0 + j + 2);
+    if (wave_needs(j + 1)) compute_tile(st1, j + 1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
@@ -529,22 +542,24 @@ hipError_t launch_fp8_prepare(const PrepareArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <bool CAUSAL, bool VARLEN>
+template <bool CAUSAL, bool VARLEN, bool WINDOW = false>
 hipError_t launch_fp8_mode(const FwdArgs& a, hipStream_t stream) {
   constexpr int kWaves = [] { int w[] = {ATTN_FP8_SHAPE}; return w[0]; }();
   const int br = 32 * kWaves;
   const int nqb = (a.N + br - 1) / br;
   const long long grid = (long long)nqb * a.Hq * a.B;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_fp8_kernel<ATTN_FP8_SHAPE, CAUSAL, VARLEN>), dim3((unsigned)grid), dim3(64 * kWaves), 0,
+  hipLaunchKernelGGL((fwd_fp8_kernel<ATTN_FP8_SHAPE, CAUSAL, VARLEN, WINDOW>), dim3((unsigned)grid), dim3(64 * kWaves), 0,
                      stream, static_cast<const uint8_t*>(a.q), static_cast<const uint8_t*>(a.k),
                      static_cast<const uint8_t*>(a.v), a.q_scale, a.k_scale, a.v_scale,
-                     static_cast<uint16_t*>(a.o), a.lse, a.Hq, a.Hkv, a.N, a.cu_seqlens, a.B, a.alpha, nqb);
+                     static_cast<uint16_t*>(a.o), a.lse, a.Hq, a.Hkv, a.N, a.cu_seqlens, a.B, a.alpha, nqb, a.window);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream) {
   const bool varlen = a.cu_seqlens != nullptr;
+  if (a.window > 0)
+    return varlen ? launch_fp8_mode<true, true, true>(a, stream) : launch_fp8_mode<true, false, true>(a, stream);
   if (a.causal) return varlen ? launch_fp8_mode<true, true>(a, stream) : launch_fp8_mode<true, false>(a, stream);
   return varlen ? launch_fp8_mode<false, true>(a, stream) : launch_fp8_mode<false, false>(a, stream);
 }

@@ -17,6 +17,7 @@ struct FwdArgs {
   const int* cu_seqlens;      // device int32 [B+1] or nullptr
   int d;
   int causal;
+  int window;                 // causal sliding window of this many keys, or 0 for none
   float alpha;
   const float* q_scale;       // fp8 only
   const float* k_scale;

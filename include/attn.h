@@ -94,6 +94,22 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              hipStream_t stream);
 
 /*
+ * attn_fwd_window -- causal attention inside a sliding window (the guijiagi overview's
+ * "sliding window attention" paragraph: attention taken only inside a local window, read as
+ * the causal window of the W most recent positions).
+ *
+ * Query i of a sequence sees keys j with i - window < j <= i: the window keys ending at
+ * itself.  window must be >= 1 (ATTN_ERR_INVALID otherwise); window >= N is plain causal
+ * attention.  Every other argument, layout, limit and status is that of attn_fwd with
+ * causal = 1; bf16, fp16 and e4m3 inputs are accepted alike.
+ */
+int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int Hq, int Hkv, int N, const int* cu_seqlens,
+                    int d, int window, float alpha, attn_dtype_t dtype,
+                    const float* q_scale, const float* k_scale, const float* v_scale,
+                    hipStream_t stream);
+
+/*
  * attn_fp8_prepare -- the FP8 pre-pass (digest section 3.5: block quantisation and
  * incoherent processing; power-of-two block scales as the blog article's FP8 section
  * requires).

@@ -57,7 +57,8 @@ class AttnInputs:
     """One seeded attention problem.
 
     ``q``, ``k``, ``v`` hold storage bit patterns: uint16 for bf16/fp16.  ``dtype`` is
-    "bf16" or "fp16".  ``cu_seqlens`` is None for dense inputs.
+    "bf16" or "fp16".  ``cu_seqlens`` is None for dense inputs.  ``window`` > 0 (with causal)
+    asks for a sliding window: query i sees keys i-window+1 .. i.
     """
 
     q: np.ndarray
@@ -73,6 +74,7 @@ class AttnInputs:
     cu_seqlens: np.ndarray | None = None
     seed: int = 0
     meta: dict = field(default_factory=dict)
+    window: int = 0
 
     @property
     def alpha(self) -> float:
@@ -88,8 +90,12 @@ class AttnInputs:
         return np.diff(self.cu_seqlens.astype(np.int64))
 
     def flops(self) -> float:
-        """4 * Hq * d * (sum over sequences of n^2), halved when causal."""
+        """4 * Hq * d * (sum over sequences of n^2), halved when causal; with a window W the
+        causal count n^2/2 loses the (n-W)^2/2 pairs at least W apart (same convention)."""
         n = self.seqlens().astype(np.float64)
+        if self.causal and self.window > 0:
+            far = np.maximum(n - self.window, 0.0)
+            return 4.0 * self.Hq * self.d * float(np.sum(n * n - far * far)) / 2.0
         f = 4.0 * self.Hq * self.d * float(np.sum(n * n))
         return f / 2.0 if self.causal else f
 

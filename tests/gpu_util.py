@@ -39,7 +39,7 @@ def run_gpu(inp: seeded_inputs.AttnInputs):
 
     q, k, v, cu = to_device(inp)
     o, lse = ea.attention(q, k, v, causal=inp.causal, alpha=inp.alpha, cu_seqlens=cu,
-                          max_seqlen=inp.N if cu is not None else None)
+                          max_seqlen=inp.N if cu is not None else None, window=inp.window or None)
     torch.cuda.synchronize()
     return o.double().cpu().numpy(), lse.double().cpu().numpy()
 
@@ -50,7 +50,8 @@ def widened(inp):
 
 def oracle_full(inp):
     q, k, v = widened(inp)
-    return oracle.attention(q, k, v, causal=inp.causal, alpha=inp.alpha, cu_seqlens=inp.cu_seqlens)
+    return oracle.attention(q, k, v, causal=inp.causal, alpha=inp.alpha, cu_seqlens=inp.cu_seqlens,
+                            window=inp.window)
 
 
 def sample_rows(inp, n: int, seed: int = 0):

@@ -19,7 +19,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = ea.header_functions()
-    assert set(names) == {"attn_fwd", "attn_fp8_prepare", "attn_fp8_prepare_ex", "attn_strerror"}
+    assert set(names) == {"attn_fwd", "attn_fwd_window", "attn_fp8_prepare", "attn_fp8_prepare_ex", "attn_strerror"}
     out = subprocess.run(["nm", "-D", "--defined-only", ea.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
@@ -76,6 +76,29 @@ def fwd(lib, q=A, k=A, v=A, o=A, lse=A, B=1, Hq=2, Hkv=2, N=128, cu=None, d=128,
 ])
 def test_fwd_validation(lib, kw, status):
     assert fwd(lib, **kw) == status
+
+
+def fwd_window(lib, window, q=A, k=A, v=A, o=A, lse=A, B=1, Hq=2, Hkv=2, N=128, cu=None, d=128, alpha=0.125,
+               dtype=ea.ATTN_BF16, qs=None, ks=None, vs=None):
+    P = ctypes.c_void_p
+    return lib.attn_fwd_window(P(q), P(k), P(v), P(o), P(lse), B, Hq, Hkv, N, P(cu) if cu else None, d, window,
+                               alpha, dtype, P(qs) if qs else None, P(ks) if ks else None, P(vs) if vs else None,
+                               None)
+
+
+@pytest.mark.parametrize("window,kw,status", [
+    (0, {}, ea.ATTN_ERR_INVALID),
+    (-3, {}, ea.ATTN_ERR_INVALID),
+    (16, dict(q=0), ea.ATTN_ERR_INVALID),
+    (16, dict(alpha=float("nan")), ea.ATTN_ERR_INVALID),
+    (16, dict(Hq=3, Hkv=2), ea.ATTN_ERR_INVALID),
+    (16, dict(d=96), ea.ATTN_ERR_UNSUPPORTED),
+    (16, dict(dtype=ea.ATTN_FP8_E4M3), ea.ATTN_ERR_INVALID),  # no scales
+    (16, dict(dtype=ea.ATTN_FP8_E4M3, qs=A, ks=A, vs=A, d=64), ea.ATTN_ERR_UNSUPPORTED),
+    (16, dict(o=A + 2), ea.ATTN_ERR_ALIGN),
+])
+def test_fwd_window_validation(lib, window, kw, status):
+    assert fwd_window(lib, window, **kw) == status
 
 
 def prep(lib, q=A, k=A, v=A, q8=A, k8=A, v8=A, qs=A, ks=A, vs=A, B=1, Hq=2, Hkv=2, N=128, d=128):

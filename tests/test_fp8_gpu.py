@@ -133,7 +133,7 @@ def gpu_fp8_attention(inp, signs, per_tensor=False):
 
     q8, k8, v8, qs, ks, vs = gpu_prepare(inp, signs, per_tensor)
     o, lse = ea.attention(q8, k8, v8, causal=inp.causal, alpha=inp.alpha, q_scale=qs, k_scale=ks, v_scale=vs,
-                          **_packed(inp))
+                          window=inp.window or None, **_packed(inp))
     torch.cuda.synchronize()
     return o.double().cpu().numpy(), lse.double().cpu().numpy(), (q8, k8, v8, qs, ks, vs)
 
@@ -150,7 +150,7 @@ def _three_errors(inp, o, lse, prep, heads, tokens):
     else:
         qd, kd, vd = (ofp8.dequantize_varlen(c, sc, cu) for c, sc in ((q8, qs), (k8, ks), (v8, vs)))
     q, k, v = gu.widened(inp)
-    kw = dict(causal=inp.causal, alpha=inp.alpha, cu_seqlens=cu)
+    kw = dict(causal=inp.causal, alpha=inp.alpha, cu_seqlens=cu, window=inp.window)
     o_ref, lse_ref = oracle.attention_rows(q, k, v, heads, tokens, **kw)
     o_dq, lse_dq = oracle.attention_rows(qd, kd, vd, heads, tokens, **kw)
     o_s, lse_s = gu.gpu_rows(inp, o, lse, heads, tokens)
