@@ -34,6 +34,15 @@ Readings where the pages leave a step open:
   quantisation (and the baseline of its Table 3 ablation), uses one exponent for a whole
   tensor, chosen by the same rule from the tensor's largest magnitude; the scale arrays keep
   their per-block shape with every entry equal.
+* Rotary position embedding before the rotation (the digest's section 3.5 fuses the pre-pass
+  into the rotary embedding that precedes attention; the guijiagi overview's "fusion with
+  RoPE" paragraph).  The pages do not define the embedding, so the original RoFormer form is
+  read: features (2i, 2i+1) of the token at position m (counted from its sequence's first
+  token) are rotated by the angle whose cosine and sine the caller tabulates in fp32 at
+  [m, i].  Each output is formed as a rotary kernel working in fp32 forms it -- x0*c - x1*s
+  and x0*s + x1*c, every product and sum rounded to fp32 -- and rounded to bf16 (nearest,
+  ties to even), i.e. the bf16 tensor an unfused rotary kernel would hand on; the pre-pass
+  then proceeds on it.
 * The Hadamard sums are formed exactly (fp64 sums of bf16 values with +-1 weights are exact
   unless one row spans more than 2**38 in magnitude), so the code chosen for each element is
   the round-to-nearest-even of the exact rotated value.
@@ -175,6 +184,47 @@ def fp8_prepare(q, k, v, signs: np.ndarray | None, block: int = BLOCK, per_tenso
     v8, ev = quant(np.asarray(v, dtype=np.float64), block)
     to_scale = lambda e: np.ldexp(np.ones(e.shape, dtype=np.float32), e.astype(np.int32))
     return q8, k8, v8, to_scale(eq), to_scale(ek - shift_k), to_scale(ev)
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """float32 -> nearest bfloat16 value (ties to the even significand), returned as float32.
+    Finite inputs only: the dropped 16 bits decide the rounding of the kept 16."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    keep_lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + keep_lsb) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)
+
+
+def rope(x: np.ndarray, cos: np.ndarray, sin: np.ndarray, positions: np.ndarray) -> np.ndarray:
+    """Rotary embedding of x [..., T, H, d] (fp64 copies of bf16 values) at the given token
+    positions [T] (broadcast over leading axes), with fp32 tables cos, sin [>= max position + 1,
+    d/2]; returns the bf16 results as float64."""
+    x = np.asarray(x, dtype=np.float64)
+    x0 = x[..., 0::2].astype(np.float32)  # exact: bf16 values are fp32 values
+    x1 = x[..., 1::2].astype(np.float32)
+    c = np.asarray(cos, dtype=np.float32)[positions][:, None, :]  # [T, 1, d/2]
+    s = np.asarray(sin, dtype=np.float32)[positions][:, None, :]
+    r0 = (x0 * c) - (x1 * s)  # float32 operations, each rounded to nearest
+    r1 = (x0 * s) + (x1 * c)
+    out = np.empty(x.shape, dtype=np.float64)
+    out[..., 0::2] = bf16_round(r0)
+    out[..., 1::2] = bf16_round(r1)
+    return out
+
+
+def rope_prepare(q, k, v, cos, sin, signs: np.ndarray | None, per_tensor: bool = False, cu_seqlens=None,
+                 max_seqlen: int | None = None):
+    """The pre-pass with the rotary embedding first: Q and K are embedded at their positions
+    within their sequences, V is not; then :func:`fp8_prepare` (dense [B, N, H, d]) or
+    :func:`fp8_prepare_varlen` (packed [T, H, d])."""
+    if cu_seqlens is None:
+        N = np.shape(q)[1]
+        pos = np.arange(N)
+        return fp8_prepare(rope(q, cos, sin, pos), rope(k, cos, sin, pos), v, signs, per_tensor=per_tensor)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    pos = np.concatenate([np.arange(cu[b + 1] - cu[b]) for b in range(len(cu) - 1)]).astype(np.int64)
+    return fp8_prepare_varlen(rope(q, cos, sin, pos), rope(k, cos, sin, pos), v, cu, max_seqlen, signs,
+                              per_tensor=per_tensor)
 
 
 def fp8_prepare_varlen(q, k, v, cu_seqlens, max_seqlen: int, signs: np.ndarray | None, block: int = BLOCK,

@@ -38,6 +38,12 @@ MUTATIONS = {
     "varlen_blocks_not_restarted": ("c, e = quantize_blocks(seq, block, floor)",
                                     "c, e = quantize_blocks(y[None, :cu[b + 1]], block, floor)\n"
                                     "                c = c[:, cu[b]:]"),
+    "rope_sin_sign": ("r0 = (x0 * c) - (x1 * s)", "r0 = (x0 * c) + (x1 * s)"),
+    "rope_half_split_pairs": ("x0 = x[..., 0::2].astype(np.float32)", "x0 = x[..., 1::2].astype(np.float32)"),
+    "rope_positions_from_packed_axis": (
+        "pos = np.concatenate([np.arange(cu[b + 1] - cu[b]) for b in range(len(cu) - 1)]).astype(np.int64)",
+        "pos = np.arange(cu[-1])"),
+    "bf16_ties_up": ("r = ((u + 0x7FFF + keep_lsb) >> 16) << 16", "r = ((u + 0x8000) >> 16) << 16"),
     "signed_zero_kept": ("-int(exps[b, h, j])) + 0.0)", "-int(exps[b, h, j])))"),
     "dequantize_next_block": ("tok_blk = np.arange(N) // block", "tok_blk = np.minimum(np.arange(N) // block + 1, "
                               "scales.shape[2] - 1)"),

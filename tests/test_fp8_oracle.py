@@ -10,6 +10,9 @@
   digest's section 3.5).
 * Hand-computed codes where block and per-tensor scaling differ; the floor that keeps every
   scale a normal fp32 power of two; a zero block does not pull a tensor's scale to 1.
+* The rotary embedding read into the fused pre-pass: bf16 rounding against torch's, a
+  hand-computed rotation of interleaved pairs, closeness to the exact rotation, the relative-
+  position property of RoFormer angles, and positions restarting at every packed sequence.
 * The outlier mixture of the paper's numerical-error experiment (section 4.3): its second
   moment and outlier count, and that the rotation lowers the error that quantising such
   inputs costs (the direction of the paper's Table 3).
@@ -249,6 +252,87 @@ def test_varlen_prepare_is_per_sequence(per_tensor):
     ref = fp8.fp8_prepare(q[None, :70], k[None, :70], v[None, :70], signs, per_tensor=per_tensor)
     for i in range(6):
         assert np.array_equal(one[i], ref[i][0] if i < 3 else ref[i])
+
+
+def test_bf16_round_matches_torch():
+    """Nearest-even rounding to bf16, ties included, agrees with torch's CPU conversion."""
+    rng = np.random.default_rng(30)
+    x = (rng.standard_normal(200000) * np.exp(rng.uniform(-20, 20, 200000))).astype(np.float32)
+    # exact ties: the dropped 16 bits are 0x8000, the kept significand bit odd or even
+    expo = rng.integers(100, 150, 4000, dtype=np.uint32) << 23
+    ties = (expo | (rng.integers(0, 128, 4000, dtype=np.uint32) << 16) | np.uint32(0x8000)).view(np.float32)
+    for v in (x, ties, -ties):
+        want = torch.from_numpy(v).to(torch.bfloat16).float().numpy()
+        assert np.array_equal(fp8.bf16_round(v), want)
+
+
+def test_rope_hand_computed():
+    """Pairs (0,1) and (2,3) use table columns 0 and 1 at the token's position: with
+    cos = (1/2, 0), sin = (3/4, 1) at position 1, (1, 0, 1/2, 2) becomes (1/2, 3/4, -2, 1/2);
+    position 0 (cos 1, sin 0) leaves the row alone."""
+    x = np.array([[[1.0, 0.0, 0.5, 2.0]], [[1.0, 0.0, 0.5, 2.0]]])  # [T=2, H=1, d=4]
+    cos = np.array([[1.0, 1.0], [0.5, 0.0]], dtype=np.float32)
+    sin = np.array([[0.0, 0.0], [0.75, 1.0]], dtype=np.float32)
+    out = fp8.rope(x, cos, sin, np.array([0, 1]))
+    assert out[0, 0].tolist() == [1.0, 0.0, 0.5, 2.0]
+    assert out[1, 0].tolist() == [0.5, 0.75, -2.0, 0.5]
+
+
+def _rope_tables(P, d, base=10000.0):
+    ang = np.arange(P)[:, None] * base ** (-np.arange(0, d, 2) / d)[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32), ang
+
+
+def test_rope_close_to_exact_rotation_and_relative():
+    """Against the rotation in fp64: within the fp32 operations' rounding plus half a bf16 ulp.
+    With RoFormer angles m * base^(-2i/d), <R_m q, R_n k> depends on m - n only (up to the
+    same rounding)."""
+    rng = np.random.default_rng(31)
+    T, d = 64, 16
+    x = fp8.bf16_round(rng.standard_normal((T, 1, d)).astype(np.float32)).astype(np.float64)
+    cos, sin, ang = _rope_tables(T, d)
+    out = fp8.rope(x, cos, sin, np.arange(T))
+    c, s_ = cos.astype(np.float64)[:, None, :], sin.astype(np.float64)[:, None, :]
+    exact0 = x[..., 0::2] * c - x[..., 1::2] * s_
+    exact1 = x[..., 0::2] * s_ + x[..., 1::2] * c
+    mag = np.abs(x[..., 0::2]) + np.abs(x[..., 1::2])
+    for got, ex in ((out[..., 0::2], exact0), (out[..., 1::2], exact1)):
+        assert np.all(np.abs(got - ex) <= 2.0 ** -8 * np.abs(ex) + 2.0 ** -22 * mag)
+    q = fp8.bf16_round(rng.standard_normal((1, 1, d)).astype(np.float32)).astype(np.float64)
+    k = fp8.bf16_round(rng.standard_normal((1, 1, d)).astype(np.float32)).astype(np.float64)
+    dots = {}
+    for m, n in ((5, 2), (20, 17), (40, 37), (9, 9), (30, 30)):
+        qm = fp8.rope(q, cos, sin, np.array([m]))
+        kn = fp8.rope(k, cos, sin, np.array([n]))
+        dots[(m, n)] = float(np.sum(qm * kn))
+    scale = float(np.sum(np.abs(q)) * np.max(np.abs(k)))
+    assert abs(dots[(5, 2)] - dots[(20, 17)]) < 2.0 ** -6 * scale
+    assert abs(dots[(5, 2)] - dots[(40, 37)]) < 2.0 ** -6 * scale
+    assert abs(dots[(9, 9)] - float(np.sum(q * k))) < 2.0 ** -6 * scale
+    assert abs(dots[(30, 30)] - float(np.sum(q * k))) < 2.0 ** -6 * scale
+
+
+@pytest.mark.parametrize("per_tensor", [False, True])
+def test_rope_prepare_positions_per_sequence(per_tensor):
+    """Packed sequences take positions from their own first token: the packed fused pre-pass
+    equals the dense one of each sequence alone (per block), and V is never embedded."""
+    rng = np.random.default_rng(32)
+    lengths = [70, 1, 130]
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    T, H, d = int(cu[-1]), 2, 16
+    mk = lambda: bf16_to_f64(seeded_inputs.f32_to_bf16_bits(rng.standard_normal((T, H, d)).astype(np.float32)))
+    q, k, v = mk(), mk(), mk()
+    cos, sin, _ = _rope_tables(200, d)
+    signs = seeded_inputs.hadamard_signs(d, seed=3)
+    got = fp8.rope_prepare(q, k, v, cos, sin, signs, per_tensor=per_tensor, cu_seqlens=cu, max_seqlen=200)
+    for b, n in enumerate(lengths):
+        sl = slice(cu[b], cu[b + 1])
+        want = fp8.rope_prepare(q[None, sl], k[None, sl], v[None, sl], cos, sin, signs)
+        if not per_tensor:
+            for i in range(3):
+                assert np.array_equal(got[i][sl], want[i][0]), (b, i)
+    plain = fp8.fp8_prepare_varlen(q, k, v, cu, 200, signs, per_tensor=per_tensor)
+    assert np.array_equal(got[2], plain[2]) and np.array_equal(got[5], plain[5], equal_nan=True)
 
 
 def test_mixture_inputs_moments():
