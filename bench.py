@@ -274,6 +274,23 @@ def run_fp8(args, dev, stream, workload="fp8", inp=None):
     pw, pg = timed(prep, stream, args.steps, args.warmup)
     elems = q.numel() + k.numel() + v.numel()
     prep_bytes = 2 * elems + elems + (qs.numel() + ks.numel() + vs.numel()) * 4 + inp.d
+    rope_extra = {}
+    if workload == "fp8" and inp.window == 0:
+        # the same pre-pass fused with a rotary embedding (fp32 tables [N, d/2])
+        cos, sin = (torch.from_numpy(t).to(dev) for t in si.rope_tables(inp.N, inp.d))
+
+        def rope_prep():
+            ea.attn_fp8_prepare_ex(q, k, v, q8, k8, v8, qs, ks, vs, hadamard_signs=signs, rope_cos=cos, rope_sin=sin,
+                                   stream=stream)
+
+        rw, rg = timed(rope_prep, stream, args.steps, args.warmup)
+        rbytes = prep_bytes + 2 * cos.numel() * 4
+        rope_extra = {"rope_prepare_ms": round(rw, 4),
+                      "rope_prepare_roofline": {"bound": "hbm", "achieved": round(rbytes / (rg * 1e-3) / 1e9, 1),
+                                                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                                "frac": round(rbytes / (rg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                                "bytes_per_launch": rbytes},
+                      "rope_unfused_extra_bytes": 4 * (q.numel() + k.numel())}
     extra = {"attention_only": True, "hadamard": True, "inputs_from": src,
              "prepare_ms": round(pw, 4),
              "prepare_roofline": {"bound": "hbm", "achieved": round(prep_bytes / (pg * 1e-3) / 1e9, 1),
@@ -281,7 +298,7 @@ def run_fp8(args, dev, stream, workload="fp8", inp=None):
                                   "frac": round(prep_bytes / (pg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                   "traffic": measured_traffic("fp8_prepare") if workload == "fp8" else None,
                                   "bytes_per_launch": prep_bytes},
-             "prepare_plus_attention_tflops": round(inp.flops() / ((pw + ms_wall) * 1e-3) / 1e12, 2)}
+             "prepare_plus_attention_tflops": round(inp.flops() / ((pw + ms_wall) * 1e-3) / 1e12, 2), **rope_extra}
     name = "fp8_b2_h16_n8192_d128" if workload == "fp8" else f"fp8_{src}"
     if inp.window:
         name = f"fp8_window{inp.window}_b1_h16_n16384_d128"

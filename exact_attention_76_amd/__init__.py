@@ -64,7 +64,7 @@ def load_library(build_if_missing: bool = True):
     lib.attn_fwd_window.restype = I
     lib.attn_fp8_prepare.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, P]
     lib.attn_fp8_prepare.restype = I
-    lib.attn_fp8_prepare_ex.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, P, I, P, I, P]
+    lib.attn_fp8_prepare_ex.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, P, I, P, P, P, I, P]
     lib.attn_fp8_prepare_ex.restype = I
     lib.attn_strerror.argtypes = [I]
     lib.attn_strerror.restype = ctypes.c_char_p
@@ -289,24 +289,36 @@ def attn_fp8_prepare(q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, *, hadamard
 
 
 def attn_fp8_prepare_ex(q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, *, scaling: int = ATTN_FP8_SCALE_BLOCK,
-                        cu_seqlens=None, max_seqlen: int | None = None, hadamard_signs=None, stream=None) -> None:
+                        cu_seqlens=None, max_seqlen: int | None = None, rope_cos=None, rope_sin=None,
+                        hadamard_signs=None, stream=None) -> None:
     """:func:`attn_fp8_prepare` for the dense or the packed layout (``cu_seqlens`` int32 [B+1]
     on the GPU, q [T, Hq, d], k/v [T, Hkv, d], ``max_seqlen`` >= the longest sequence; scales
     [B, H, ceil(max_seqlen/64)]), with ``scaling`` = ATTN_FP8_SCALE_BLOCK (one scale per
-    64-token block) or ATTN_FP8_SCALE_TENSOR (one scale per tensor, in every block entry)."""
+    64-token block) or ATTN_FP8_SCALE_TENSOR (one scale per tensor, in every block entry), and
+    optionally fused with a rotary embedding (``rope_cos``, ``rope_sin``: float32 [P, d/2] with
+    P >= the sequence length, position = token index within its sequence)."""
     dev, (B, Hq, Hkv, N, d) = _prepare_call(q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, hadamard_signs,
                                             cu_seqlens, max_seqlen, "attn_fp8_prepare_ex")
+    if (rope_cos is None) != (rope_sin is None):
+        raise ValueError("rope_cos and rope_sin come together")
+    if rope_cos is not None:
+        for nm, t in (("rope_cos", rope_cos), ("rope_sin", rope_sin)):
+            _check_tensor(t, nm)
+            if t.dtype != torch.float32 or t.dim() != 2 or t.shape[1] != d // 2 or t.shape[0] < N:
+                raise ValueError(f"{nm} must be float32 [P >= {N}, {d // 2}]")
+        _one_device((("q", q), ("rope_cos", rope_cos), ("rope_sin", rope_sin)))
     lib = load_library()
     with torch.cuda.device(dev):
         st = lib.attn_fp8_prepare_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale),
                                      _ptr(k_scale), _ptr(v_scale), B, Hq, Hkv, N, _ptr(cu_seqlens), d,
-                                     _ptr(hadamard_signs), int(scaling), _stream_handle(stream, dev))
+                                     _ptr(rope_cos), _ptr(rope_sin), _ptr(hadamard_signs), int(scaling),
+                                     _stream_handle(stream, dev))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fp8_prepare_ex")
 
 
 def fp8_prepare(q, k, v, *, hadamard_signs=None, per_tensor: bool = False, cu_seqlens=None,
-                max_seqlen: int | None = None, stream=None):
+                max_seqlen: int | None = None, rope_cos=None, rope_sin=None, stream=None):
     """Allocate the e4m3 tensors (as uint8 codes) and scales and run the pre-pass, with one scale
     per 64-token block (:func:`attn_fp8_prepare`) or, with ``per_tensor``, one per tensor;
     ``cu_seqlens`` / ``max_seqlen`` select the packed layout (:func:`attn_fp8_prepare_ex`)."""
@@ -324,11 +336,11 @@ def fp8_prepare(q, k, v, *, hadamard_signs=None, per_tensor: bool = False, cu_se
     qs = torch.empty((B, Hq, nblk), dtype=torch.float32, device=dev)
     ks = torch.empty((B, Hkv, nblk), dtype=torch.float32, device=dev)
     vs = torch.empty((B, Hkv, nblk), dtype=torch.float32, device=dev)
-    if per_tensor or cu_seqlens is not None:
+    if per_tensor or cu_seqlens is not None or rope_cos is not None:
         attn_fp8_prepare_ex(q, k, v, q8, k8, v8, qs, ks, vs,
                             scaling=ATTN_FP8_SCALE_TENSOR if per_tensor else ATTN_FP8_SCALE_BLOCK,
-                            cu_seqlens=cu_seqlens, max_seqlen=max_seqlen, hadamard_signs=hadamard_signs,
-                            stream=stream)
+                            cu_seqlens=cu_seqlens, max_seqlen=max_seqlen, rope_cos=rope_cos, rope_sin=rope_sin,
+                            hadamard_signs=hadamard_signs, stream=stream)
     else:
         attn_fp8_prepare(q, k, v, q8, k8, v8, qs, ks, vs, hadamard_signs=hadamard_signs, stream=stream)
     return q8, k8, v8, qs, ks, vs

@@ -97,23 +97,26 @@ int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float*
 int attn_fp8_prepare(const void* q, const void* k, const void* v, void* q8, void* k8, void* v8,
                      float* q_scale, float* k_scale, float* v_scale, int B, int Hq, int Hkv, int N, int d,
                      const signed char* hadamard_signs, hipStream_t stream) {
-  return attn_fp8_prepare_ex(q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, B, Hq, Hkv, N, nullptr, d,
-                             hadamard_signs, ATTN_FP8_SCALE_BLOCK, stream);
+  return attn_fp8_prepare_ex(q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, B, Hq, Hkv, N, nullptr, d, nullptr,
+                             nullptr, hadamard_signs, ATTN_FP8_SCALE_BLOCK, stream);
 }
 
 int attn_fp8_prepare_ex(const void* q, const void* k, const void* v, void* q8, void* k8, void* v8, float* q_scale,
                         float* k_scale, float* v_scale, int B, int Hq, int Hkv, int N, const int* cu_seqlens, int d,
-                        const signed char* hadamard_signs, attn_fp8_scaling_t scaling, hipStream_t stream) {
+                        const float* rope_cos, const float* rope_sin, const signed char* hadamard_signs,
+                        attn_fp8_scaling_t scaling, hipStream_t stream) {
   if (scaling != ATTN_FP8_SCALE_BLOCK && scaling != ATTN_FP8_SCALE_TENSOR) return ATTN_ERR_INVALID;
+  if ((rope_cos == nullptr) != (rope_sin == nullptr)) return ATTN_ERR_INVALID;
   int rc = validate_common(q, k, v, q8, k8, B, Hq, Hkv, N);
   if (rc != ATTN_OK) return rc;
   if (!v8 || !q_scale || !k_scale || !v_scale) return ATTN_ERR_INVALID;
   if (d != 128) return ATTN_ERR_UNSUPPORTED;
   if ((long long)B * Hq * ((N + 63) / 64) > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;  // grid size
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q8) || !aligned16(k8) || !aligned16(v8))
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q8) || !aligned16(k8) || !aligned16(v8) ||
+      !aligned16(rope_cos) || !aligned16(rope_sin))
     return ATTN_ERR_ALIGN;
   attn::PrepareArgs a{q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, B, Hq, Hkv, N, d, cu_seqlens, hadamard_signs,
-                      scaling == ATTN_FP8_SCALE_TENSOR};
+                      scaling == ATTN_FP8_SCALE_TENSOR, rope_cos, rope_sin};
   return status_of(attn::launch_fp8_prepare(a, stream));
 }
 

@@ -13,6 +13,8 @@
 //     registers, two across the lane quad), so the rotated values are exact; the block's
 //     largest magnitude picks the exponent and every element is rounded to e4m3 from its exact
 //     fp64 value (fp64 -> fp32 rounded to odd, then the hardware's nearest-even conversion).
+//     With rotary tables, Q and K are first embedded (fp32, rounded to bf16) in registers, so
+//     the fused pre-pass reads and writes what the plain one does plus the tables.
 //     Per-tensor scaling (the usual practice that block quantisation replaces) takes three
 //     launches: the same kernel writes each block's exponent into its scale slot, one
 //     workgroup per tensor reduces the slots to the tensor's exponent and writes its scale
@@ -63,6 +65,7 @@ struct PrepTensor {
   int H;
   int rotate;         // multiply by diag(signs) * Hadamard first
   int scale_shift;    // log2 of the extra divisor folded into the scale (7 for rotated K)
+  int embed;          // Q or K: takes the rotary embedding when there is one
 };
 
 // fp64 -> fp32 rounded to odd: the value truncated toward zero, its last bit set when the
@@ -95,12 +98,45 @@ enum PrepPass : int {
   kPrepTensorCodes = 2,  // per-tensor, last pass: codes with the exponent the slot now holds
 };
 
+// Rotary embedding of one lane's 32 features (16 interleaved pairs, pairs 16p .. 16p+15) at
+// position pos: fp32 products and sums rounded one by one (no fused multiply-add), then bf16
+// (nearest even) -- the tensor an unfused fp32 rotary kernel would write.
+__device__ __forceinline__ void rope32(double* y, const float* __restrict__ cos_row,
+                                       const float* __restrict__ sin_row) {
+#pragma clang fp contract(off)
+  float c[16], s[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u32x4 a = reinterpret_cast<const u32x4*>(cos_row)[i];
+    const u32x4 b = reinterpret_cast<const u32x4*>(sin_row)[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      c[4 * i + e] = __uint_as_float(a[e]);
+      s[4 * i + e] = __uint_as_float(b[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float x0 = (float)y[2 * e], x1 = (float)y[2 * e + 1];  // exact: bf16 values
+    const float r0 = x0 * c[e] - x1 * s[e];  // contraction is off in this function
+    const float r1 = x0 * s[e] + x1 * c[e];
+    const f32x2 r = {r0, r1};
+    const uint32_t packed = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
+    y[2 * e] = (double)__uint_as_float(packed << 16);
+    y[2 * e + 1] = (double)__uint_as_float(packed & 0xFFFF0000u);
+  }
+}
+
 // Dense: B sequences of N tokens.  Packed (cu != nullptr): sequence b holds tokens cu[b] ..
-// cu[b+1]-1 (at most N of them), and its blocks count from its first token.
-template <int PASS>
+// cu[b+1]-1 (at most N of them), and its blocks count from its first token.  ROPE: Q and K are
+// first embedded at each token's position in its sequence with the fp32 tables rope_cos,
+// rope_sin [positions, 64].
+template <int PASS, bool ROPE>
 __global__ __launch_bounds__(256) void fp8_prepare_kernel(PrepTensor t0, PrepTensor t1, PrepTensor t2, int B, int N,
                                                           int nblk, const int* __restrict__ cu,
-                                                          const signed char* __restrict__ signs) {
+                                                          const signed char* __restrict__ signs,
+                                                          const float* __restrict__ rope_cos,
+                                                          const float* __restrict__ rope_sin) {
   const PrepTensor t = blockIdx.y == 0 ? t0 : (blockIdx.y == 1 ? t1 : t2);
   const int H = t.H;
   if ((int)blockIdx.x >= B * H * nblk) return;  // this tensor has fewer heads than the grid
@@ -134,6 +170,12 @@ __global__ __launch_bounds__(256) void fp8_prepare_kernel(PrepTensor t0, PrepTen
         y[8 * c + 2 * e] = (double)__uint_as_float(w[e] << 16);
         y[8 * c + 2 * e + 1] = (double)__uint_as_float(w[e] & 0xFFFF0000u);
       }
+    }
+  }
+  if constexpr (ROPE) {
+    if (t.embed) {
+      const int64_t row = (int64_t)(valid ? token : 0) * 64 + 16 * p;
+      rope32(y, rope_cos + row, rope_sin + row);
     }
   }
   if (t.rotate) {
@@ -517,29 +559,36 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 3 : 1)) void fwd_fp8_kern
 
 }  // namespace
 
-hipError_t launch_fp8_prepare(const PrepareArgs& a, hipStream_t stream) {
+template <bool ROPE>
+hipError_t launch_prepare_passes(const PrepareArgs& a, hipStream_t stream) {
   const int nblk = (a.N + 63) / 64;
+  // Q and K take the rotary embedding (if any) and the Hadamard rotation (if signs are given)
   const bool rot = a.signs != nullptr;
-  PrepTensor tq{static_cast<const uint16_t*>(a.q), static_cast<uint8_t*>(a.q8), a.q_scale, a.Hq, rot, 0};
-  PrepTensor tk{static_cast<const uint16_t*>(a.k), static_cast<uint8_t*>(a.k8), a.k_scale, a.Hkv, rot, rot ? 7 : 0};
-  PrepTensor tv{static_cast<const uint16_t*>(a.v), static_cast<uint8_t*>(a.v8), a.v_scale, a.Hkv, 0, 0};
+  PrepTensor tq{static_cast<const uint16_t*>(a.q), static_cast<uint8_t*>(a.q8), a.q_scale, a.Hq, rot, 0, 1};
+  PrepTensor tk{static_cast<const uint16_t*>(a.k), static_cast<uint8_t*>(a.k8), a.k_scale, a.Hkv, rot, rot ? 7 : 0, 1};
+  PrepTensor tv{static_cast<const uint16_t*>(a.v), static_cast<uint8_t*>(a.v8), a.v_scale, a.Hkv, 0, 0, 0};
   const long long grid = (long long)a.B * a.Hq * nblk;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const dim3 g((unsigned)grid, 3);
   if (!a.per_tensor) {
-    hipLaunchKernelGGL(fp8_prepare_kernel<kPrepBlock>, dim3((unsigned)grid, 3), dim3(256), 0, stream, tq, tk, tv, a.B,
-                       a.N, nblk, a.cu_seqlens, a.signs);
+    hipLaunchKernelGGL((fp8_prepare_kernel<kPrepBlock, ROPE>), g, dim3(256), 0, stream, tq, tk, tv, a.B, a.N, nblk,
+                       a.cu_seqlens, a.signs, a.rope_cos, a.rope_sin);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(fp8_prepare_kernel<kPrepTensorScan>, dim3((unsigned)grid, 3), dim3(256), 0, stream, tq, tk, tv,
-                     a.B, a.N, nblk, a.cu_seqlens, a.signs);
+  hipLaunchKernelGGL((fp8_prepare_kernel<kPrepTensorScan, ROPE>), g, dim3(256), 0, stream, tq, tk, tv, a.B, a.N, nblk,
+                     a.cu_seqlens, a.signs, a.rope_cos, a.rope_sin);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(fp8_tensor_scale_kernel, dim3(3), dim3(1024), 0, stream, tq, tk, tv, a.B, nblk);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(fp8_prepare_kernel<kPrepTensorCodes>, dim3((unsigned)grid, 3), dim3(256), 0, stream, tq, tk, tv,
-                     a.B, a.N, nblk, a.cu_seqlens, a.signs);
+  hipLaunchKernelGGL((fp8_prepare_kernel<kPrepTensorCodes, ROPE>), g, dim3(256), 0, stream, tq, tk, tv, a.B, a.N,
+                     nblk, a.cu_seqlens, a.signs, a.rope_cos, a.rope_sin);
   return hipGetLastError();
+}
+
+hipError_t launch_fp8_prepare(const PrepareArgs& a, hipStream_t stream) {
+  return a.rope_cos != nullptr ? launch_prepare_passes<true>(a, stream) : launch_prepare_passes<false>(a, stream);
 }
 
 template <bool CAUSAL, bool VARLEN, bool WINDOW = false>

@@ -44,6 +44,8 @@ struct PrepareArgs {
   const int* cu_seqlens;      // device int32 [B+1] or nullptr
   const signed char* signs;
   int per_tensor;             // one scale per tensor instead of one per 64-token block
+  const float* rope_cos;      // rotary tables [positions, d/2] fp32, or nullptr
+  const float* rope_sin;
 };
 
 hipError_t launch_fp8_prepare(const PrepareArgs& a, hipStream_t stream);

@@ -145,7 +145,7 @@ typedef enum {
 
 /*
  * attn_fp8_prepare_ex -- attn_fp8_prepare with every option: the packed variable-length
- * layout and a choice of scale granularity.
+ * layout, a choice of scale granularity and a fused rotary embedding.
  *
  * cu_seqlens: NULL for the dense layout, or the packed layout of attn_fwd: int32 [B + 1] on the
  *   device, q [T, Hq, d], k and v [T, Hkv, d], N >= the longest sequence.  Blocks then count
@@ -161,12 +161,23 @@ typedef enum {
  *   takes three kernel launches on `stream` and uses the scale arrays as working storage
  *   between them: their contents are defined only once all three have run.  Any other value
  *   returns ATTN_ERR_INVALID.
+ * rope_cos, rope_sin: NULL (both), or fp32 device tables [P, d/2] with P >= N, 16-byte
+ *   aligned: the pre-pass is then fused with a rotary position embedding (the digest's section
+ *   3.5 fuses quantisation and the Hadamard rotation into the rotary embedding; the guijiagi
+ *   overview's RoPE-fusion paragraph).  Before anything else, features (2i, 2i+1) of every
+ *   q and k token at position m of its sequence (m counted from the sequence's first token)
+ *   become x0*c - x1*s and x0*s + x1*c with c = rope_cos[m][i], s = rope_sin[m][i], each
+ *   product and sum rounded to fp32 and the results rounded to bf16 (nearest even): the bf16
+ *   tensors an unfused fp32 rotary kernel would write, which never reach memory here.  v is
+ *   not embedded.  Only one of the two NULL returns ATTN_ERR_INVALID; misaligned tables
+ *   ATTN_ERR_ALIGN.
  * Everything else is as for attn_fp8_prepare.
  */
 int attn_fp8_prepare_ex(const void* q, const void* k, const void* v,
                         void* q8, void* k8, void* v8,
                         float* q_scale, float* k_scale, float* v_scale,
                         int B, int Hq, int Hkv, int N, const int* cu_seqlens, int d,
+                        const float* rope_cos, const float* rope_sin,
                         const signed char* hadamard_signs, attn_fp8_scaling_t scaling,
                         hipStream_t stream);
 

@@ -31,6 +31,7 @@ __all__ = [
     "fp8_inputs",
     "mixture_inputs",
     "hadamard_signs",
+    "rope_tables",
     "CONFIGS",
 ]
 
@@ -196,6 +197,13 @@ def mixture_inputs(B: int, N: int, H: int, d: int, *, seed: int, outlier_prob: f
     inp.meta["outlier_prob"] = outlier_prob
     inp.meta["outlier_std"] = outlier_std
     return inp
+
+
+def rope_tables(positions: int, d: int, base: float = 10000.0):
+    """fp32 cos and sin tables [positions, d/2] of RoFormer's angles m * base^(-2i/d), formed in
+    float64 and rounded once to float32 (inputs of the fused rotary pre-pass)."""
+    ang = np.arange(positions, dtype=np.float64)[:, None] * base ** (-np.arange(0, d, 2, dtype=np.float64) / d)
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
 
 
 def hadamard_signs(d: int, seed: int = 55) -> np.ndarray:

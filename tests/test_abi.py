@@ -122,10 +122,11 @@ def test_prepare_validation(lib, kw, status):
 
 
 def prep_ex(lib, scaling, q=A, k=A, v=A, q8=A, k8=A, v8=A, qs=A, ks=A, vs=A, B=1, Hq=2, Hkv=2, N=128, cu=None,
-            d=128):
+            d=128, rc=None, rs=None):
     P = ctypes.c_void_p
     return lib.attn_fp8_prepare_ex(P(q), P(k), P(v), P(q8), P(k8), P(v8), P(qs), P(ks), P(vs),
-                                   B, Hq, Hkv, N, P(cu) if cu else None, d, None, scaling, None)
+                                   B, Hq, Hkv, N, P(cu) if cu else None, d, P(rc) if rc else None,
+                                   P(rs) if rs else None, None, scaling, None)
 
 
 @pytest.mark.parametrize("scaling,kw,status", [
@@ -140,6 +141,9 @@ def prep_ex(lib, scaling, q=A, k=A, v=A, q8=A, k8=A, v8=A, qs=A, ks=A, vs=A, B=1
     (ea.ATTN_FP8_SCALE_BLOCK, dict(cu=A, d=64), ea.ATTN_ERR_UNSUPPORTED),
     (ea.ATTN_FP8_SCALE_TENSOR, dict(cu=A, k8=A + 8), ea.ATTN_ERR_ALIGN),
     (ea.ATTN_FP8_SCALE_BLOCK, dict(B=1 << 15, Hq=1 << 10, Hkv=1 << 10, N=1 << 15), ea.ATTN_ERR_UNSUPPORTED),
+    (ea.ATTN_FP8_SCALE_BLOCK, dict(rc=A), ea.ATTN_ERR_INVALID),  # cos without sin
+    (ea.ATTN_FP8_SCALE_BLOCK, dict(rs=A), ea.ATTN_ERR_INVALID),
+    (ea.ATTN_FP8_SCALE_TENSOR, dict(rc=A + 4, rs=A), ea.ATTN_ERR_ALIGN),
 ])
 def test_prepare_ex_validation(lib, scaling, kw, status):
     assert prep_ex(lib, scaling, **kw) == status

@@ -6,7 +6,8 @@
   the same for attn_fp8_prepare_scaling's per-tensor scales, and for blocks so small that their
   scales sit on the 2^-126 floor, or all zero.
 * the same for packed variable-length sequences (attn_fp8_prepare_ex), blocks restarting at
-  every sequence, with per-block and per-tensor scales.
+  every sequence, with per-block and per-tensor scales, and for the pre-pass fused with a
+  rotary embedding (fp32 tables), dense and packed.
 * attn_fwd on e4m3 inputs -- dense and packed, causal or not, grouped-query heads -- against
   the fp64 oracle run on the *unquantised* bf16 inputs (the
   error measure of the FlashAttention-3 digest's section 3.5 / Table 3): O RMSE <= 3e-2, or the
@@ -37,18 +38,23 @@ def _packed(inp):
     return dict(cu_seqlens=torch.from_numpy(inp.cu_seqlens.astype(np.int32)).cuda(), max_seqlen=inp.N)
 
 
-def gpu_prepare(inp, signs, per_tensor=False):
+def gpu_prepare(inp, signs, per_tensor=False, tables=None):
     import exact_attention_76_amd as ea
 
     q, k, v = (_dev_bf16(getattr(inp, n)) for n in "qkv")
     sg = None if signs is None else torch.from_numpy(signs).cuda()
-    out = ea.fp8_prepare(q, k, v, hadamard_signs=sg, per_tensor=per_tensor, **_packed(inp))
+    rope = {} if tables is None else dict(rope_cos=torch.from_numpy(tables[0]).cuda(),
+                                          rope_sin=torch.from_numpy(tables[1]).cuda())
+    out = ea.fp8_prepare(q, k, v, hadamard_signs=sg, per_tensor=per_tensor, **_packed(inp), **rope)
     torch.cuda.synchronize()
     return out
 
 
-def oracle_prepare(inp, signs, per_tensor=False):
+def oracle_prepare(inp, signs, per_tensor=False, tables=None):
     q, k, v = (oracle.bf16_to_f64(getattr(inp, n)) for n in "qkv")
+    if tables is not None:
+        return ofp8.rope_prepare(q, k, v, tables[0], tables[1], signs, per_tensor=per_tensor,
+                                 cu_seqlens=inp.cu_seqlens, max_seqlen=inp.N)
     if inp.cu_seqlens is not None:
         return ofp8.fp8_prepare_varlen(q, k, v, inp.cu_seqlens, inp.N, signs, per_tensor=per_tensor)
     return ofp8.fp8_prepare(q, k, v, signs, per_tensor=per_tensor)
@@ -303,3 +309,46 @@ def test_fp8_attention_full_varlen_gqa():
     inp = si.CONFIGS["gqa_varlen_causal_hq32_hkv8_d128"]()
     gu.say("fp8 attention full packed GQA causal")
     check_fp8(*_full(inp, 2048))
+
+
+# ---- pre-pass fused with the rotary embedding ----------------------------------------------------
+
+@pytest.mark.parametrize("per_tensor", [False, True])
+@pytest.mark.parametrize("rotate", [True, False])
+@pytest.mark.parametrize("packed", [False, True])
+def test_prepare_rope_bit_exact(packed, rotate, per_tensor):
+    inp = _varlen_small(True, 620) if packed else si.dense_inputs(2, 130, 4, 128, Hkv=2, seed=621)
+    inp.q = si.f32_to_bf16_bits(si.bf16_bits_to_f32(inp.q) * np.float32(5.0))
+    tables = si.rope_tables(inp.N + 7, 128)
+    signs = si.hadamard_signs(128, seed=55) if rotate else None
+    gu.say("fp8 prepare + rotary", packed, rotate, per_tensor)
+    _assert_prepare_equal(gpu_prepare(inp, signs, per_tensor, tables), oracle_prepare(inp, signs, per_tensor, tables),
+                          f"rotary prepare packed={packed} rotate={rotate} per_tensor={per_tensor}")
+
+
+def test_prepare_rope_bit_exact_full_workload():
+    inp = si.CONFIGS["fp8_b2_h16_n8192_d128"]()
+    tables = si.rope_tables(inp.N, 128)
+    signs = si.hadamard_signs(128, seed=55)
+    gu.say("fp8 prepare + rotary full workload")
+    _assert_prepare_equal(gpu_prepare(inp, signs, False, tables), oracle_prepare(inp, signs, False, tables),
+                          "rotary prepare full")
+
+
+def test_fp8_attention_after_rope():
+    """Attention on the fused pre-pass's output against fp64 attention of the embedded bf16
+    Q, K (the oracle's rotary embedding) and V, causal, every row."""
+    import exact_attention_76_amd as ea
+
+    inp = si.dense_inputs(1, 300, 4, 128, causal=True, seed=622)
+    tables = si.rope_tables(inp.N, 128)
+    gu.say("fp8 attention after rotary pre-pass")
+    prep = gpu_prepare(inp, si.hadamard_signs(128, seed=55), False, tables)
+    o, lse = ea.attention(*prep[:3], causal=True, alpha=inp.alpha, q_scale=prep[3], k_scale=prep[4], v_scale=prep[5])
+    torch.cuda.synchronize()
+    o, lse = o.double().cpu().numpy(), lse.double().cpu().numpy()
+    pos = np.arange(inp.N)
+    ref = si.AttnInputs(*(si.f32_to_bf16_bits(ofp8.rope(oracle.bf16_to_f64(getattr(inp, n)), *tables, pos)
+                                             .astype(np.float32)) for n in "qk"), inp.v, "bf16",
+                        inp.B, inp.N, inp.Hq, inp.Hkv, inp.d, True, None, inp.seed)
+    check_fp8(*_three_errors(ref, o, lse, prep, *_all_rows(ref)))
