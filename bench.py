@@ -14,6 +14,8 @@ sweep's aggregate (total FLOPs over total time).  ``--workload`` selects the oth
           (Hadamard rotation + block quantisation, HBM-bound) is timed separately
   fp8_causal  the same kernel causal, on the bf16 causal d=128 workload's inputs
   fp8_varlen  the same kernel on the packed causal GQA workload's inputs
+  bwd     backward pass (attn_bwd: D pre-pass, dK/dV, dQ) on the headline inputs (B=1 N=16384,
+          non-causal) and the causal d=128 inputs (B=2 N=8192); FLOPs = 2.5 x the forward's
   window  causal sliding window of 4096 keys, B=1 N=16384 H=16 d=128 (the headline's inputs), bf16
           then e4m3; FLOPs count the visible pairs, n^2/2 - (n-W)^2/2 per head
   ceiling the matrix-core ceiling the attention kernels run against: back-to-back
@@ -84,7 +86,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mha16k", choices=["mha16k", "sweep", "causal", "varlen", "fp8", "fp8_causal",
-                                                              "fp8_varlen", "window", "ceiling"])
+                                                              "fp8_varlen", "window", "bwd", "ceiling"])
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -306,6 +308,28 @@ def run_fp8(args, dev, stream, workload="fp8", inp=None):
                 traffic=measured_traffic("fp8_attention") if workload == "fp8" else None, launches=launches)
 
 
+def run_bwd(args, name, inp, dev, stream):
+    """The backward pass on inputs resident in HBM (Q, K, V, O, L from the forward, dO)."""
+    import torch
+
+    import exact_attention_76_amd as ea
+    import seeded_inputs as si
+
+    q, k, v = (to_dev(getattr(inp, n), inp.dtype, dev) for n in "qkv")
+    do = to_dev(si.output_gradient(inp, 9), inp.dtype, dev)
+    o, lse = ea.attention(q, k, v, causal=inp.causal, alpha=inp.alpha, stream=stream)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(inp.B * inp.Hq * inp.N, dtype=torch.float32, device=dev)
+
+    def step():
+        ea.attn_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, causal=inp.causal, alpha=inp.alpha, stream=stream)
+
+    ms_wall, ms_gpu = timed(step, stream, args.steps, args.warmup)
+    launches = per_launch(step, stream, args.steps)
+    return line(args, name, inp, 2.5 * inp.flops(), ms_wall, ms_gpu, inp.dtype, launches=launches,
+                extra={"pass": "backward", "flops_rule": "2.5 x forward (five products)"})
+
+
 def run_ceiling(args, dev, stream):
     import ctypes
 
@@ -400,6 +424,9 @@ def main():
             out = [run_16bit(args, n, si.CONFIGS[n](), dev, stream)]
         elif args.workload in FP8_WORKLOADS:
             out = [run_fp8(args, dev, stream, args.workload)]
+        elif args.workload == "bwd":
+            out = [run_bwd(args, "bwd_" + n, si.CONFIGS[n](), dev, stream)
+                   for n in ("mha_n16384_b1_h16_d128", "causal_b2_h16_n8192_d128")]
         elif args.workload == "window":
             out = [run_16bit(args, f"window{WINDOW}_b1_h16_n16384_d128", window_inputs(), dev, stream),
                    run_fp8(args, dev, stream, "mha_n16384_b1_h16_d128", inp=window_inputs())]

@@ -13,7 +13,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJ_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ["api.hip", "attn_fwd.hip", "fp8.hip"]
+SOURCES = ["api.hip", "attn_fwd.hip", "attn_bwd.hip", "fp8.hip"]
 CEILING_LIB = os.path.join(PKG, "libceiling.so")
 CEILING_SOURCES = ["ceiling.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

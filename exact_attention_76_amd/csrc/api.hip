@@ -94,6 +94,30 @@ int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float*
              k_scale, v_scale, stream);
 }
 
+size_t attn_bwd_workspace_bytes(int B, int Hq, int N) {
+  if (B <= 0 || Hq <= 0 || N <= 0) return 0;
+  return (size_t)B * (size_t)Hq * (size_t)N * sizeof(float);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+             void* dq, void* dk, void* dv, float* workspace, int B, int Hq, int Hkv, int N, const int* cu_seqlens,
+             int d, int causal, float alpha, attn_dtype_t dtype, hipStream_t stream) {
+  int rc = validate_common(q, k, v, o, lse, B, Hq, Hkv, N);
+  if (rc != ATTN_OK) return rc;
+  if (!dout || !dq || !dk || !dv || !workspace) return ATTN_ERR_INVALID;
+  if (!(isfinite(alpha) && alpha > 0.f)) return ATTN_ERR_INVALID;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  // the kernels address one head's Q (and dO) rows with 32-bit byte offsets
+  if ((long long)N * Hq * d * 2 > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+    return ATTN_ERR_ALIGN;
+  attn::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, cu_seqlens, d, causal, alpha};
+  return status_of(attn::launch_bwd_16bit(a, dtype == ATTN_BF16, stream));
+}
+
 int attn_fp8_prepare(const void* q, const void* k, const void* v, void* q8, void* k8, void* v8,
                      float* q_scale, float* k_scale, float* v_scale, int B, int Hq, int Hkv, int N, int d,
                      const signed char* hadamard_signs, hipStream_t stream) {

@@ -1,0 +1,477 @@
+// attn_bwd.hip -- backward pass of exact attention for gfx950, 16-bit inputs (bf16 / fp16).
+//
+// Method (FlashAttention-3 pages, zenmind digest section 4, data path step 5: a pre-processing
+// step forms D = rowsum(dO * O), and the backward pass recomputes P from the stored L instead of
+// keeping it): with S = alpha Q K^T and P = exp(S - L),
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dQ = alpha dS K,  dK = alpha dS^T Q,
+// dK and dV summed over the query heads of a key/value group.  Five products, as the digest's
+// section 7.1 counts (2.5 x the forward FLOPs).
+//
+// gfx950 mapping (ours):
+//   * bwd_delta_kernel: D per (query, head), one 16-byte slice of dO and O per lane.
+//   * bwd_dkdv_kernel: a workgroup of four waves owns 128 keys of one (sequence, key/value head),
+//     32 per wave; its K and V rows stay in registers as matrix-instruction B operands (one key
+//     per lane column).  It walks the query tiles of every query head of the group: Q and dO
+//     tiles (and their L and D values) are copied buffer-to-LDS, two stages deep, and each
+//     tile takes S = Q K^T and dP = dO V^T (A operands read from the tile rows), P and dS in
+//     registers (the query of each accumulator row picks its L and D from LDS), then
+//     dV^T += dO^T P and dK^T += Q^T dS (A operands read transposed from the same tiles, the
+//     accumulators of P and dS fed back as B operands, as the forward pass feeds P^T).
+//   * bwd_dq_kernel: the forward pass's shape -- four waves own 128 queries, one per lane
+//     column; per key tile S^T = K Q^T and dP^T = V dO^T, dS^T in registers, dQ^T += K^T dS^T
+//     with K read transposed.  Every gradient is written once; no atomics, so the result is
+//     deterministic.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "decompose.h"
+#include "internal.h"
+#include "tile16.h"
+
+namespace attn {
+namespace {
+
+constexpr int kWaves = 4;  // waves per workgroup in both products kernels
+constexpr int kBlk = 32 * kWaves;  // keys (dK/dV) or queries (dQ) per workgroup
+constexpr int kTile = 64;  // streamed rows per tile (dQ: keys; dK/dV: queries at d = 64)
+// dK/dV at d = 128 streams 32-query tiles: its resident K, V and both accumulators leave no
+// room for the scores of 64 queries without spilling
+template <int D>
+constexpr int dkdv_tile() { return D == 128 ? 32 : 64; }
+
+// 16-bit values -> float
+template <bool BF16>
+__device__ __forceinline__ float lo16(uint32_t w) {
+  if constexpr (BF16) return __uint_as_float(w << 16);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFF));
+}
+template <bool BF16>
+__device__ __forceinline__ float hi16(uint32_t w) {
+  if constexpr (BF16) return __uint_as_float(w & 0xFFFF0000u);
+  else return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// D[row] = sum over d of dO * O for every (token, query head) row; delta has the LSE layout.
+// The grid covers B * N tokens; packed input has T = cu_seqlens[nseq] <= B * N of them.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
+                                                        float* __restrict__ delta, int Hq, int N, int B,
+                                                        const int* __restrict__ cu_seqlens) {
+  constexpr int LPR = D / 8;  // lanes per row, 8 elements each
+  const int64_t T = cu_seqlens ? (int64_t)cu_seqlens[B] : (int64_t)B * N;
+  const int64_t rows = T * Hq;
+  const int packed = cu_seqlens != nullptr;
+  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LPR;
+  const int part = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(o + row * D + 8 * part);
+    const u32x4 g = *reinterpret_cast<const u32x4*>(dout + row * D + 8 * part);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc += lo16<BF16>(a[e]) * lo16<BF16>(g[e]) + hi16<BF16>(a[e]) * hi16<BF16>(g[e]);
+  }
+#pragma unroll
+  for (int m = 1; m < LPR; m <<= 1) acc += __shfl_xor(acc, m);
+  if (row < rows && part == 0) {
+    const int64_t t = row / Hq;
+    const int h = (int)(row % Hq);
+    const int64_t idx = packed ? (int64_t)h * T + t : ((t / N) * Hq + h) * N + t % N;
+    delta[idx] = acc;
+  }
+}
+
+// Operand read offsets inside a 16-bit tile (tile16.h layout), lane part.
+//   rows: A operand from tile rows 32*cb + l32, k-step st over d (chunk 2*st + hi)
+//   tr:   A operand of a transposed tile (d rows, tile rows as k) by ds_read_b64_tr_b16
+template <int D>
+__device__ __forceinline__ void operand_offsets(int lane, int* koff, int* vtoff) {
+  constexpr int NCH = D / 8;
+  const int l32 = lane & 31, hi = lane >> 5;
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+    koff[e] = 16 * ((l32 >> 4) * 16 * NCH + (2 * e + hi) * 16 + ((lane & 15) ^ (4 * (2 * e + hi))));
+  const int G = lane >> 4, r = (lane >> 2) & 3, c = lane & 3;
+#pragma unroll
+  for (int rd = 0; rd < 2; ++rd) {
+    const int chunk = 2 * (G & 1) + (c >> 1);
+    const int rowm = 4 * (G >> 1) + 8 * rd + r;
+    vtoff[rd] = 16 * (chunk * 16 + (rowm ^ (4 * chunk))) + 8 * (c & 1);
+  }
+}
+
+// C (32 x 32 per block cb) += tile rows (32*cb ..) x frag: one block per 32 tile rows.
+template <int D, bool BF16, int NB>
+__device__ __forceinline__ void rows_product(const char* tile, const int* koff, const u32x4* frag, f32x16* acc) {
+  constexpr int NCH = D / 8, KS_D = D / 16;
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) {
+    acc[cb] = f32x16{};
+#pragma unroll
+    for (int st = 0; st < KS_D; ++st) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(tile + koff[st & 1] + cb * 512 * NCH + 512 * (st & ~1));
+      acc[cb] = mma32<BF16>(a, frag[st], acc[cb]);
+    }
+  }
+}
+
+// acc^T (D x 32) += tile^T (D x 16 rows of k-step st) x pf: the transposed product of one k-step.
+template <int D, bool BF16>
+__device__ __forceinline__ void tr_product_step(const char* tile, const int* vtoff, int st, u32x4 pf, f32x16* acc) {
+  constexpr int NCH = D / 8, NB_D = D / 32;
+#pragma unroll
+  for (int db = 0; db < NB_D; ++db) {
+    const int imm = st * 256 * NCH + db * 1024;
+    const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, tile + vtoff[0] + imm));
+    const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, tile + vtoff[1] + imm));
+    const u32x2 a0 = __builtin_bit_cast(u32x2, t0), a1 = __builtin_bit_cast(u32x2, t1);
+    acc[db] = mma32<BF16>(u32x4{a0[0], a0[1], a1[0], a1[1]}, pf, acc[db]);
+  }
+}
+
+// k-step st of a 32-row accumulator block pair, packed as the B operand (registers 8*(st%2) ..
+// of block st/2).
+template <bool BF16>
+__device__ __forceinline__ u32x4 pack_step(const f32x16* x, int st) {
+  const int cb = st >> 1, base = (st & 1) * 8;
+  return u32x4{pack2<BF16>(x[cb][base + 0], x[cb][base + 1]), pack2<BF16>(x[cb][base + 2], x[cb][base + 3]),
+               pack2<BF16>(x[cb][base + 4], x[cb][base + 5]), pack2<BF16>(x[cb][base + 6], x[cb][base + 7])};
+}
+
+// Accumulator row held by register r of a 32x32 block: 8*(r/4) + 4*hi + r%4.
+__device__ __forceinline__ int acc_row(int r, int hi) { return 8 * (r >> 2) + 4 * hi + (r & 3); }
+
+// Store a D x 32 transposed accumulator (lane = token column) as 16-bit rows, times scale.
+template <int D, bool BF16>
+__device__ __forceinline__ void store_rows(uint16_t* dst, const f32x16* acc, float scale, int hi) {
+  constexpr int NB_D = D / 32;
+  uint16_t* p = dst + 4 * hi;
+#pragma unroll
+  for (int db = 0; db < NB_D; ++db)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      u32x2 pr = {pack2<BF16>(acc[db][4 * gq + 0] * scale, acc[db][4 * gq + 1] * scale),
+                  pack2<BF16>(acc[db][4 * gq + 2] * scale, acc[db][4 * gq + 3] * scale)};
+      *reinterpret_cast<u32x2*>(p + db * 32 + gq * 8) = pr;
+    }
+}
+
+template <int D, int ROWS>
+__device__ __forceinline__ int copy_offset(int wave, int lane, int rowbytes) {
+  constexpr int NI = ROWS * D * 2 / 1024 / kWaves;
+  int row, chunk;
+  tile_row_chunk<D>(wave * NI * 64 + lane, row, chunk);
+  return row * rowbytes + chunk * 16;
+}
+
+// ---- dK, dV -------------------------------------------------------------------------------------
+template <int D, bool BF16, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(64 * kWaves, 1) void bwd_dkdv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int Hq, int Hkv, int N, const int* __restrict__ cu_seqlens,
+    int nseq, float alpha, int num_kblocks) {
+  constexpr int NCH = D / 8, KS_D = D / 16, NB_D = D / 32;
+  constexpr int TQ = dkdv_tile<D>();  // queries per tile
+  constexpr int TILE = TQ * D * 2;
+  constexpr int NI = TILE / 1024 / kWaves, IPB = NCH / 4;
+  constexpr int NB = TQ / 32, KS = TQ / 16;  // query blocks and k-steps of one tile
+  static_assert(NI * kWaves * 1024 == TILE && (NI % IPB == 0 || NI < IPB), "tile shape");
+  __shared__ __attribute__((aligned(1024))) char qt0[TILE];
+  __shared__ __attribute__((aligned(1024))) char qt1[TILE];
+  __shared__ __attribute__((aligned(1024))) char gt0[TILE];
+  __shared__ __attribute__((aligned(1024))) char gt1[TILE];
+  __shared__ __attribute__((aligned(1024))) float ld0[2][256];  // L and D of a tile (64 used each)
+  __shared__ __attribute__((aligned(1024))) float ld1[2][256];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  // ---- which (sequence, key/value head, key block): heads of the same sequence on one XCD ----
+  int kb, g, b;
+  decompose<false>(blockIdx.x, num_kblocks, Hkv, Hkv, nseq, kb, g, b);
+  int seq_start, n;
+  if constexpr (VARLEN) {
+    seq_start = cu_seqlens[b];
+    n = cu_seqlens[b + 1] - seq_start;
+    if (n > N) n = N;
+  } else {
+    seq_start = b * N;
+    n = N;
+  }
+  const int k0 = kb * kBlk;
+  if (k0 >= n) return;
+  const int G = Hq / Hkv;
+  const int kw = k0 + wave * 32;  // first key of this wave
+  const int kj = kw + l32;        // this lane's key
+
+  // K and V of this lane's key as B operands: d = 16*st + 8*hi .. +7
+  u32x4 kf[KS_D], vf[KS_D];
+  {
+    const int row = kj < n ? kj : n - 1;
+    const int64_t off = ((int64_t)(seq_start + row) * Hkv + g) * D + 8 * hi;
+#pragma unroll
+    for (int s = 0; s < KS_D; ++s) {
+      kf[s] = *reinterpret_cast<const u32x4*>(k + off + 16 * s);
+      vf[s] = *reinterpret_cast<const u32x4*>(v + off + 16 * s);
+    }
+  }
+  int koff[2], vtoff[2];
+  operand_offsets<D>(lane, koff, vtoff);
+
+  const int rowbytes = Hq * D * 2;  // Q and dO rows of one head
+  const int voff = copy_offset<D, TQ>(wave, lane, rowbytes);
+  const int blk_bytes = 16 * rowbytes;
+  const int nbytes = (n - 1) * rowbytes + D * 2;
+  // causal: the first query tile that holds a query >= the block's first key
+  const int t_first = CAUSAL ? k0 / TQ : 0;
+  const int ntiles = (n + TQ - 1) / TQ - t_first;
+  const int total = G * ntiles;  // (head, tile) steps
+  const int64_t lstride = VARLEN ? (int64_t)cu_seqlens[nseq] : (int64_t)N;
+
+  // step s: head g*G + s / ntiles, query tile t_first + s % ntiles
+  auto issue = [&](char* qdst, char* gdst, float (*lddst)[256], int s) {
+    const int h = g * G + s / ntiles;
+    const int q0 = (t_first + s % ntiles) * TQ;
+    const int64_t base = ((int64_t)(seq_start + q0) * Hq + h) * D * 2;
+    const int rem = nbytes - q0 * rowbytes;
+    copy_rows_to_lds<NI, IPB>(reinterpret_cast<const char*>(q) + base, rem, qdst + wave * NI * 1024, voff,
+                              blk_bytes);
+    copy_rows_to_lds<NI, IPB>(reinterpret_cast<const char*>(dout) + base, rem, gdst + wave * NI * 1024, voff,
+                              blk_bytes);
+    if (wave == 0) {  // L and D of the tile's queries (TQ floats each; queries past n read as 0)
+      const int64_t lrow = VARLEN ? (int64_t)h * lstride + seq_start + q0 : ((int64_t)b * Hq + h) * N + q0;
+      const int bytes = (n - q0) * 4;
+#if defined(__HIP_DEVICE_COMPILE__)
+      __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc((void*)(lse + lrow), 0, bytes, 0x00020000);
+      __amdgpu_buffer_rsrc_t rd = __builtin_amdgcn_make_buffer_rsrc((void*)(delta + lrow), 0, bytes, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, LDS_PTR(void, lddst[0]), 16, 16 * lane, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, LDS_PTR(void, lddst[1]), 16, 16 * lane, 0, 0, 0);
+#endif
+    }
+  };
+
+  f32x16 dka[NB_D], dva[NB_D];
+#pragma unroll
+  for (int i = 0; i < NB_D; ++i) dka[i] = dva[i] = f32x16{};
+  const float c = alpha * kLog2e;
+
+  auto compute = [&](const char* qt, const char* gt, float (*ldt)[256], int s) {
+    const int q0 = (t_first + s % ntiles) * TQ;
+    if (CAUSAL && q0 + TQ - 1 < kw) return;  // every query of the tile is before this wave's keys
+    f32x16 sc[NB], dp[NB];
+    rows_product<D, BF16, NB>(qt, koff, kf, sc);  // S = Q K^T (rows: queries; column: this lane's key)
+    rows_product<D, BF16, NB>(gt, koff, vf, dp);  // dP = dO V^T
+    const bool mask = (q0 + TQ > n) || (CAUSAL && q0 < kw + 31);
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int row0 = 32 * cb + 8 * r4 + 4 * hi;  // four consecutive queries of this register group
+        const float4 L = *reinterpret_cast<const float4*>(&ldt[0][row0]);
+        const float4 Dv = *reinterpret_cast<const float4*>(&ldt[1][row0]);
+        const float Lr[4] = {L.x, L.y, L.z, L.w}, Dr[4] = {Dv.x, Dv.y, Dv.z, Dv.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e;
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cb][r], c, -Lr[e] * kLog2e));
+          if (mask) {
+            const int qi = q0 + row0 + e;
+            if (qi >= n || (CAUSAL && qi < kj)) p = 0.f;
+          }
+          sc[cb][r] = p;
+          dp[cb][r] = p * (dp[cb][r] - Dr[e]);
+        }
+      }
+#pragma unroll
+    for (int st = 0; st < KS; ++st) {
+      tr_product_step<D, BF16>(gt, vtoff, st, pack_step<BF16>(sc, st), dva);  // dV^T += dO^T P
+      tr_product_step<D, BF16>(qt, vtoff, st, pack_step<BF16>(dp, st), dka);  // dK^T += Q^T dS
+    }
+  };
+
+  issue(qt0, gt0, ld0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int s = 0; s < total; s += 2) {
+    if (s + 1 < total) issue(qt1, gt1, ld1, s + 1);
+    compute(qt0, gt0, ld0, s);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (s + 1 >= total) break;
+    if (s + 2 < total) issue(qt0, gt0, ld0, s + 2);
+    compute(qt1, gt1, ld1, s + 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  if (kj < n) {
+    const int64_t off = ((int64_t)(seq_start + kj) * Hkv + g) * D;
+    store_rows<D, BF16>(dk + off, dka, alpha, hi);
+    store_rows<D, BF16>(dv + off, dva, 1.f, hi);
+  }
+}
+
+// ---- dQ -----------------------------------------------------------------------------------------
+template <int D, bool BF16, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(64 * kWaves, 2) void bwd_dq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
+    uint16_t* __restrict__ dq, int Hq, int Hkv, int N, const int* __restrict__ cu_seqlens, int nseq, float alpha,
+    int num_qblocks) {
+  constexpr int NCH = D / 8, KS_D = D / 16, NB_D = D / 32;
+  constexpr int TILE = kTile * D * 2;
+  constexpr int NI = TILE / 1024 / kWaves, IPB = NCH / 4;
+  constexpr int NB = kTile / 32, KS = kTile / 16;
+  static_assert(NI * kWaves * 1024 == TILE && (NI % IPB == 0 || NI < IPB), "tile shape");
+  __shared__ __attribute__((aligned(1024))) char kt0[TILE];
+  __shared__ __attribute__((aligned(1024))) char kt1[TILE];
+  __shared__ __attribute__((aligned(1024))) char vt0[TILE];
+  __shared__ __attribute__((aligned(1024))) char vt1[TILE];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+
+  int qb, h, b;
+  decompose<CAUSAL>(blockIdx.x, num_qblocks, Hq, Hkv, nseq, qb, h, b);
+  int seq_start, n;
+  if constexpr (VARLEN) {
+    seq_start = cu_seqlens[b];
+    n = cu_seqlens[b + 1] - seq_start;
+    if (n > N) n = N;
+  } else {
+    seq_start = b * N;
+    n = N;
+  }
+  const int q0 = qb * kBlk;
+  if (q0 >= n) return;
+  const int g = h / (Hq / Hkv);
+  const int qw = q0 + wave * 32;
+  const int qi = qw + l32;
+
+  // Q and dO of this lane's query (B operands), its L and D
+  u32x4 qf[KS_D], gf[KS_D];
+  float Lc = 0.f, Dq = 0.f;
+  {
+    const int row = qi < n ? qi : n - 1;
+    const int64_t off = ((int64_t)(seq_start + row) * Hq + h) * D + 8 * hi;
+#pragma unroll
+    for (int s = 0; s < KS_D; ++s) {
+      qf[s] = *reinterpret_cast<const u32x4*>(q + off + 16 * s);
+      gf[s] = *reinterpret_cast<const u32x4*>(dout + off + 16 * s);
+    }
+    const int64_t idx = VARLEN ? (int64_t)h * cu_seqlens[nseq] + seq_start + row : ((int64_t)b * Hq + h) * N + row;
+    Lc = lse[idx] * kLog2e;
+    Dq = delta[idx];
+  }
+  int koff[2], vtoff[2];
+  operand_offsets<D>(lane, koff, vtoff);
+
+  const int rowbytes = Hkv * D * 2;
+  const int voff = copy_offset<D, kTile>(wave, lane, rowbytes);
+  const int blk_bytes = 16 * rowbytes;
+  const char* kbase = reinterpret_cast<const char*>(k) + ((int64_t)seq_start * Hkv + g) * D * 2;
+  const char* vbase = reinterpret_cast<const char*>(v) + ((int64_t)seq_start * Hkv + g) * D * 2;
+  const int nbytes = (n - 1) * rowbytes + D * 2;
+  auto issue = [&](char* kdst, char* vdst, int tile) {
+    const int off = tile * kTile * rowbytes;
+    copy_rows_to_lds<NI, IPB>(kbase + off, nbytes - off, kdst + wave * NI * 1024, voff, blk_bytes);
+    copy_rows_to_lds<NI, IPB>(vbase + off, nbytes - off, vdst + wave * NI * 1024, voff, blk_bytes);
+  };
+  const int kv_end = CAUSAL ? min(n, q0 + kBlk) : n;
+  const int ntiles = (kv_end + kTile - 1) / kTile;
+
+  f32x16 dqa[NB_D];
+#pragma unroll
+  for (int i = 0; i < NB_D; ++i) dqa[i] = f32x16{};
+  const float c = alpha * kLog2e;
+
+  auto compute = [&](const char* kt, const char* vt, int j) {
+    const int j0 = j * kTile;
+    if (CAUSAL && j0 > qw + 31) return;  // the tile lies wholly after this wave's queries
+    f32x16 sc[NB], dp[NB];
+    rows_product<D, BF16, NB>(kt, koff, qf, sc);  // S^T = K Q^T (rows: keys; column: this lane's query)
+    rows_product<D, BF16, NB>(vt, koff, gf, dp);  // dP^T = V dO^T
+    const bool mask = (j0 + kTile > n) || (CAUSAL && j0 + kTile - 1 > qw);
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cb][r], c, -Lc));
+        if (mask) {
+          const int key = j0 + 32 * cb + acc_row(r, hi);
+          if (key >= n || (CAUSAL && key > qi)) p = 0.f;
+        }
+        dp[cb][r] = p * (dp[cb][r] - Dq);
+      }
+#pragma unroll
+    for (int st = 0; st < KS; ++st) tr_product_step<D, BF16>(kt, vtoff, st, pack_step<BF16>(dp, st), dqa);
+  };
+
+  issue(kt0, vt0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int j = 0; j < ntiles; j += 2) {
+    if (j + 1 < ntiles) issue(kt1, vt1, j + 1);
+    compute(kt0, vt0, j);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (j + 1 >= ntiles) break;
+    if (j + 2 < ntiles) issue(kt0, vt0, j + 2);
+    compute(kt1, vt1, j + 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+
+  if (qi < n) store_rows<D, BF16>(dq + ((int64_t)(seq_start + qi) * Hq + h) * D, dqa, alpha, hi);
+}
+
+template <int D, bool BF16, bool CAUSAL, bool VARLEN>
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
+  const int nblk = (a.N + kBlk - 1) / kBlk;
+  const long long grid_kv = (long long)nblk * a.Hkv * a.B, grid_q = (long long)nblk * a.Hq * a.B;
+  if (grid_q > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  // delta: one row per (token, query head); the grid covers the B * N tokens packed input can hold
+  const int64_t blocks = ((int64_t)a.B * a.N * a.Hq * (D / 8) + 255) / 256;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((bwd_delta_kernel<D, BF16>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout), a.workspace, a.Hq, a.N,
+                     a.B, a.cu_seqlens);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16, CAUSAL, VARLEN>), dim3((unsigned)grid_kv), dim3(64 * kWaves), 0, stream,
+                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                     static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), a.lse, a.workspace,
+                     static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), a.Hq, a.Hkv, a.N, a.cu_seqlens, a.B,
+                     a.alpha, nblk);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, BF16, CAUSAL, VARLEN>), dim3((unsigned)grid_q), dim3(64 * kWaves), 0, stream,
+                     static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                     static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), a.lse, a.workspace,
+                     static_cast<uint16_t*>(a.dq), a.Hq, a.Hkv, a.N, a.cu_seqlens, a.B, a.alpha, nblk);
+  return hipGetLastError();
+}
+
+template <int D, bool BF16>
+hipError_t launch_bwd_modes(const BwdArgs& a, hipStream_t stream) {
+  const bool varlen = a.cu_seqlens != nullptr;
+  if (a.causal) return varlen ? launch_bwd<D, BF16, true, true>(a, stream) : launch_bwd<D, BF16, true, false>(a, stream);
+  return varlen ? launch_bwd<D, BF16, false, true>(a, stream) : launch_bwd<D, BF16, false, false>(a, stream);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_16bit(const BwdArgs& a, bool is_bf16, hipStream_t stream) {
+  switch (a.d) {
+    case 64: return is_bf16 ? launch_bwd_modes<64, true>(a, stream) : launch_bwd_modes<64, false>(a, stream);
+    case 128: return is_bf16 ? launch_bwd_modes<128, true>(a, stream) : launch_bwd_modes<128, false>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace attn

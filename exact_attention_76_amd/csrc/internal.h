@@ -30,6 +30,27 @@ hipError_t launch_fwd_16bit(const FwdArgs& a, bool is_bf16, hipStream_t stream);
 // e4m3 inputs with per-block scales; d == 128; dense or packed, causal or not.
 hipError_t launch_fwd_fp8(const FwdArgs& a, hipStream_t stream);
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* workspace;           // fp32, B * Hq * N entries (D = rowsum(dO * O), LSE layout)
+  int B, Hq, Hkv, N;          // N: sequence length (dense) or longest sequence (packed)
+  const int* cu_seqlens;      // device int32 [B+1] or nullptr
+  int d;
+  int causal;
+  float alpha;
+};
+
+// 16-bit backward pass (bf16 when is_bf16, else fp16); d in {64, 128}.
+hipError_t launch_bwd_16bit(const BwdArgs& a, bool is_bf16, hipStream_t stream);
+
 struct PrepareArgs {
   const void* q;
   const void* k;

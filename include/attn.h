@@ -32,6 +32,7 @@
 #define LIBATTN_ATTN_H
 
 #include <hip/hip_runtime_api.h>
+#include <stddef.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -108,6 +109,35 @@ int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float*
                     int d, int window, float alpha, attn_dtype_t dtype,
                     const float* q_scale, const float* k_scale, const float* v_scale,
                     hipStream_t stream);
+
+/*
+ * attn_bwd -- gradients of attn_fwd's output with respect to q, k and v (16-bit inputs).
+ *
+ * The backward pass of the FlashAttention-3 pages (zenmind digest, section 4, data path step
+ * 5): a pre-processing step forms D = rowsum(dout * o) per (query, head), and P is recomputed
+ * from the stored lse instead of being kept.  With S = alpha q k^T and P = exp(S - lse) over
+ * the visible keys:
+ *   dv = P^T dout,  dS = P * (dout v^T - D),  dq = alpha dS k,  dk = alpha dS^T q,
+ * dk and dv summed over the query heads that share a key/value head.
+ *
+ * q, k, v, o, lse: the inputs and outputs of the attn_fwd call being differentiated (same
+ *   layouts, dtype, B, Hq, Hkv, N, cu_seqlens, d, causal and alpha).
+ * dout: gradient of the loss with respect to o, o's layout and dtype.
+ * dq, dk, dv: outputs in q's, k's and v's layouts and dtype; every element is written.
+ * workspace: fp32 device memory of at least attn_bwd_workspace_bytes(B, Hq, N) bytes, owned by
+ *   the caller; on return it holds D in lse's layout.  Nothing is allocated.
+ * d: 64 or 128; dtype: ATTN_BF16 or ATTN_FP16 (ATTN_ERR_UNSUPPORTED otherwise).
+ * Limits: N * Hq * d * 2 < 2^31 (one head's q rows addressed with 32-bit offsets).
+ * Three kernels run in order on `stream`.  Returns ATTN_OK or a negative status; on error
+ * nothing is enqueued.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, float* workspace,
+             int B, int Hq, int Hkv, int N, const int* cu_seqlens,
+             int d, int causal, float alpha, attn_dtype_t dtype, hipStream_t stream);
+
+/* Bytes of workspace attn_bwd needs (B * Hq * N floats); 0 for non-positive sizes. */
+size_t attn_bwd_workspace_bytes(int B, int Hq, int N);
 
 /*
  * attn_fp8_prepare -- the FP8 pre-pass (digest section 3.5: block quantisation and

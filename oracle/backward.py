@@ -92,15 +92,19 @@ def attention_backward(q, k, v, do, *, causal: bool = False, alpha: float | None
 
 
 def gradient_magnitudes(q, k, v, do, *, causal: bool = False, alpha: float | None = None, cu_seqlens=None,
-                        window: int = 0):
+                        window: int = 0, row_weight=None):
     """The same products taken over absolute values (|P|^T |dO| for dV, alpha |dS| |K| for dQ,
     alpha |dS|^T |Q| for dK): the size of the sums each gradient element is, against which
-    rounding errors of the factors are measured."""
+    rounding errors of the factors are measured.
+
+    With ``row_weight`` w (one value per query row and head, q's layout without d), the
+    |dS| above are replaced by |dS| + P * w: the magnitudes then also bound what an error of
+    up to w_i in D_i (which enters dS = P (dP - D)) does to dQ and dK."""
     q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
     d = q.shape[-1]
     alpha = 1.0 / np.sqrt(d) if alpha is None else float(alpha)
 
-    def seq(q, k, v, do):
+    def seq(q, k, v, do, w):
         n, Hq, _ = q.shape
         G = Hq // k.shape[1]
         mq, mk, mv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
@@ -116,18 +120,21 @@ def gradient_magnitudes(q, k, v, do, *, causal: bool = False, alpha: float | Non
                 P = E / np.sum(E, axis=1, keepdims=True)
                 dP = dO @ V.T
                 dS = np.abs(P * (dP - np.sum(P * dP, axis=1, keepdims=True)))
+                if w is not None:
+                    dS = dS + P * w[rows, h][:, None]
                 mv[:, g, :] += P.T @ np.abs(dO)
                 mq[rows, h, :] = alpha * (dS @ np.abs(K))
                 mk[:, g, :] += alpha * (dS.T @ np.abs(Q))
         return mq, mk, mv
 
+    w = None if row_weight is None else np.asarray(row_weight, dtype=np.float64)
     if cu_seqlens is None:
-        outs = [seq(q[b], k[b], v[b], do[b]) for b in range(q.shape[0])]
+        outs = [seq(q[b], k[b], v[b], do[b], None if w is None else w[b]) for b in range(q.shape[0])]
         return tuple(np.stack([o[i] for o in outs]) for i in range(3))
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     mq, mk, mv = np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)
     for b in range(len(cu) - 1):
         sl = slice(cu[b], cu[b + 1])
         if cu[b + 1] > cu[b]:
-            mq[sl], mk[sl], mv[sl] = seq(q[sl], k[sl], v[sl], do[sl])
+            mq[sl], mk[sl], mv[sl] = seq(q[sl], k[sl], v[sl], do[sl], None if w is None else w[sl])
     return mq, mk, mv

@@ -32,6 +32,7 @@ __all__ = [
     "mixture_inputs",
     "hadamard_signs",
     "rope_tables",
+    "output_gradient",
     "CONFIGS",
 ]
 
@@ -197,6 +198,12 @@ def mixture_inputs(B: int, N: int, H: int, d: int, *, seed: int, outlier_prob: f
     inp.meta["outlier_prob"] = outlier_prob
     inp.meta["outlier_std"] = outlier_std
     return inp
+
+
+def output_gradient(inp: AttnInputs, seed: int) -> np.ndarray:
+    """dO for a backward pass: i.i.d. N(0, 1) in the layout of Q (= O), rounded to inp.dtype."""
+    rng = np.random.default_rng(seed)
+    return _to_storage(rng.standard_normal(inp.q.shape, dtype=np.float32), inp.dtype)
 
 
 def rope_tables(positions: int, d: int, base: float = 10000.0):

@@ -19,7 +19,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = ea.header_functions()
-    assert set(names) == {"attn_fwd", "attn_fwd_window", "attn_fp8_prepare", "attn_fp8_prepare_ex", "attn_strerror"}
+    assert set(names) == {"attn_fwd", "attn_fwd_window", "attn_bwd", "attn_bwd_workspace_bytes", "attn_fp8_prepare",
+                          "attn_fp8_prepare_ex", "attn_strerror"}
     out = subprocess.run(["nm", "-D", "--defined-only", ea.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
@@ -147,3 +148,34 @@ def prep_ex(lib, scaling, q=A, k=A, v=A, q8=A, k8=A, v8=A, qs=A, ks=A, vs=A, B=1
 ])
 def test_prepare_ex_validation(lib, scaling, kw, status):
     assert prep_ex(lib, scaling, **kw) == status
+
+
+def bwd(lib, q=A, k=A, v=A, o=A, lse=A, do=A, dq=A, dk=A, dv=A, ws=A, B=1, Hq=2, Hkv=2, N=128, cu=None, d=128,
+        causal=0, alpha=0.125, dtype=ea.ATTN_BF16):
+    P = ctypes.c_void_p
+    return lib.attn_bwd(P(q), P(k), P(v), P(o), P(lse), P(do), P(dq), P(dk), P(dv), P(ws), B, Hq, Hkv, N,
+                        P(cu) if cu else None, d, causal, alpha, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=0), ea.ATTN_ERR_INVALID),
+    (dict(do=0), ea.ATTN_ERR_INVALID),
+    (dict(dk=0), ea.ATTN_ERR_INVALID),
+    (dict(ws=0), ea.ATTN_ERR_INVALID),
+    (dict(N=0), ea.ATTN_ERR_INVALID),
+    (dict(Hq=3, Hkv=2), ea.ATTN_ERR_INVALID),
+    (dict(alpha=float("nan")), ea.ATTN_ERR_INVALID),
+    (dict(causal=5), ea.ATTN_ERR_INVALID),
+    (dict(d=256), ea.ATTN_ERR_UNSUPPORTED),
+    (dict(dtype=ea.ATTN_FP8_E4M3), ea.ATTN_ERR_UNSUPPORTED),
+    (dict(Hq=64, Hkv=64, N=1 << 17), ea.ATTN_ERR_UNSUPPORTED),  # one head's q rows span >= 2 GiB
+    (dict(dq=A + 2), ea.ATTN_ERR_ALIGN),
+    (dict(ws=A + 4), ea.ATTN_ERR_ALIGN),
+])
+def test_bwd_validation(lib, kw, status):
+    assert bwd(lib, **kw) == status
+
+
+def test_bwd_workspace_bytes(lib):
+    assert lib.attn_bwd_workspace_bytes(2, 16, 8192) == 2 * 16 * 8192 * 4
+    assert lib.attn_bwd_workspace_bytes(0, 16, 8192) == 0
