@@ -32,8 +32,13 @@
 namespace attn {
 namespace {
 
-constexpr int kWaves = 4;  // waves per workgroup in both products kernels
-constexpr int kBlk = 32 * kWaves;  // keys (dK/dV) or queries (dQ) per workgroup
+constexpr int kWaves = 4;  // waves per workgroup of the dQ kernel
+constexpr int kBlk = 32 * kWaves;  // queries per dQ workgroup
+#ifndef ATTN_BWD_KV_WAVES
+#define ATTN_BWD_KV_WAVES 8
+#endif
+constexpr int kKvWaves = ATTN_BWD_KV_WAVES;  // waves per dK/dV workgroup (32 keys each)
+constexpr int kKvBlk = 32 * kKvWaves;         // keys per dK/dV workgroup
 constexpr int kTile = 64;  // streamed rows per tile (dQ: keys; dK/dV: queries at d = 64)
 // dK/dV at d = 128 streams 32-query tiles: its resident K, V and both accumulators leave no
 // room for the scores of 64 queries without spilling
@@ -115,6 +120,21 @@ __device__ __forceinline__ void rows_product(const char* tile, const int* koff, 
   }
 }
 
+// acc (32 x 32) = tile rows (32 ..) x the B operand read, k-step by k-step, from row block
+// `brow` (32 rows) of another tile in the same layout: one product whose both operands are in LDS.
+template <int D, bool BF16>
+__device__ __forceinline__ void rows_product_lds(const char* tile, const int* koff, const char* btile, int brow,
+                                                 f32x16& acc) {
+  constexpr int NCH = D / 8, KS_D = D / 16;
+  acc = f32x16{};
+#pragma unroll
+  for (int st = 0; st < KS_D; ++st) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(tile + koff[st & 1] + 512 * (st & ~1));
+    const u32x4 b = *reinterpret_cast<const u32x4*>(btile + koff[st & 1] + brow * 512 * NCH + 512 * (st & ~1));
+    acc = mma32<BF16>(a, b, acc);
+  }
+}
+
 // acc^T (D x 32) += tile^T (D x 16 rows of k-step st) x pf: the transposed product of one k-step.
 template <int D, bool BF16>
 __device__ __forceinline__ void tr_product_step(const char* tile, const int* vtoff, int st, u32x4 pf, f32x16* acc) {
@@ -156,9 +176,9 @@ __device__ __forceinline__ void store_rows(uint16_t* dst, const f32x16* acc, flo
     }
 }
 
-template <int D, int ROWS>
+template <int D, int ROWS, int WAVES>
 __device__ __forceinline__ int copy_offset(int wave, int lane, int rowbytes) {
-  constexpr int NI = ROWS * D * 2 / 1024 / kWaves;
+  constexpr int NI = ROWS * D * 2 / 1024 / WAVES;
   int row, chunk;
   tile_row_chunk<D>(wave * NI * 64 + lane, row, chunk);
   return row * rowbytes + chunk * 16;
@@ -166,7 +186,7 @@ __device__ __forceinline__ int copy_offset(int wave, int lane, int rowbytes) {
 
 // ---- dK, dV -------------------------------------------------------------------------------------
 template <int D, bool BF16, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(64 * kWaves, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int Hq, int Hkv, int N, const int* __restrict__ cu_seqlens,
@@ -174,24 +194,33 @@ __global__ __launch_bounds__(64 * kWaves, 1) void bwd_dkdv_kernel(
   constexpr int NCH = D / 8, KS_D = D / 16, NB_D = D / 32;
   constexpr int TQ = dkdv_tile<D>();  // queries per tile
   constexpr int TILE = TQ * D * 2;
-  constexpr int NI = TILE / 1024 / kWaves, IPB = NCH / 4;
+  constexpr int NI = TILE / 1024 / kKvWaves, IPB = NCH / 4;
   constexpr int NB = TQ / 32, KS = TQ / 16;  // query blocks and k-steps of one tile
-  static_assert(NI * kWaves * 1024 == TILE && (NI % IPB == 0 || NI < IPB), "tile shape");
+  // d = 128: V stays in LDS (the workgroup's rows, read per k-step as the B operand of dP)
+  // instead of registers, so two waves fit on a SIMD without spilling
+  constexpr bool V_LDS = D == 128;
+  static_assert(!V_LDS || NB == 1, "dP from LDS is written for one 32-query block per tile");
+  static_assert(NI * kKvWaves * 1024 == TILE && (NI % IPB == 0 || NI < IPB), "tile shape");
   __shared__ __attribute__((aligned(1024))) char qt0[TILE];
   __shared__ __attribute__((aligned(1024))) char qt1[TILE];
   __shared__ __attribute__((aligned(1024))) char gt0[TILE];
   __shared__ __attribute__((aligned(1024))) char gt1[TILE];
   __shared__ __attribute__((aligned(1024))) float ld0[2][256];  // L and D of a tile (64 used each)
   __shared__ __attribute__((aligned(1024))) float ld1[2][256];
+  __shared__ __attribute__((aligned(1024))) char vres[V_LDS ? kKvBlk * D * 2 : 16];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
 
-  // ---- which (sequence, key/value head, key block): heads of the same sequence on one XCD ----
-  int kb, g, b;
-  decompose<false>(blockIdx.x, num_kblocks, Hkv, Hkv, nseq, kb, g, b);
+  // ---- which (sequence, key/value head, key block): heads of the same sequence on one XCD;
+  // causal: a key block sees every query from its own on, so the lowest blocks are the longest
+  // and run first (the decomposition orders blocks longest first for query blocks, i.e. highest
+  // index first; the key block index is its mirror image) ----
+  int kbd, g, b;
+  decompose<CAUSAL>(blockIdx.x, num_kblocks, Hkv, Hkv, nseq, kbd, g, b);
+  const int kb = CAUSAL ? num_kblocks - 1 - kbd : kbd;
   int seq_start, n;
   if constexpr (VARLEN) {
     seq_start = cu_seqlens[b];
@@ -201,28 +230,37 @@ __global__ __launch_bounds__(64 * kWaves, 1) void bwd_dkdv_kernel(
     seq_start = b * N;
     n = N;
   }
-  const int k0 = kb * kBlk;
+  const int k0 = kb * kKvBlk;
   if (k0 >= n) return;
   const int G = Hq / Hkv;
   const int kw = k0 + wave * 32;  // first key of this wave
   const int kj = kw + l32;        // this lane's key
 
   // K and V of this lane's key as B operands: d = 16*st + 8*hi .. +7
-  u32x4 kf[KS_D], vf[KS_D];
+  u32x4 kf[KS_D], vf[V_LDS ? 1 : KS_D];
   {
     const int row = kj < n ? kj : n - 1;
     const int64_t off = ((int64_t)(seq_start + row) * Hkv + g) * D + 8 * hi;
 #pragma unroll
     for (int s = 0; s < KS_D; ++s) {
       kf[s] = *reinterpret_cast<const u32x4*>(k + off + 16 * s);
-      vf[s] = *reinterpret_cast<const u32x4*>(v + off + 16 * s);
+      if constexpr (!V_LDS) vf[s] = *reinterpret_cast<const u32x4*>(v + off + 16 * s);
     }
+  }
+  if constexpr (V_LDS) {  // the workgroup's V rows (rows past n read as zero)
+    constexpr int NIV = kKvBlk * D * 2 / 1024 / kKvWaves;
+    const int kvrow = Hkv * D * 2;
+    int row, chunk;
+    tile_row_chunk<D>(wave * NIV * 64 + lane, row, chunk);
+    const char* vb = reinterpret_cast<const char*>(v) + ((int64_t)(seq_start + k0) * Hkv + g) * D * 2;
+    copy_rows_to_lds<NIV, NCH / 4>(vb, (n - 1 - k0) * kvrow + D * 2, vres + wave * NIV * 1024, row * kvrow + chunk * 16,
+                                   16 * kvrow);
   }
   int koff[2], vtoff[2];
   operand_offsets<D>(lane, koff, vtoff);
 
   const int rowbytes = Hq * D * 2;  // Q and dO rows of one head
-  const int voff = copy_offset<D, TQ>(wave, lane, rowbytes);
+  const int voff = copy_offset<D, TQ, kKvWaves>(wave, lane, rowbytes);
   const int blk_bytes = 16 * rowbytes;
   const int nbytes = (n - 1) * rowbytes + D * 2;
   // causal: the first query tile that holds a query >= the block's first key
@@ -263,7 +301,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void bwd_dkdv_kernel(
     if (CAUSAL && q0 + TQ - 1 < kw) return;  // every query of the tile is before this wave's keys
     f32x16 sc[NB], dp[NB];
     rows_product<D, BF16, NB>(qt, koff, kf, sc);  // S = Q K^T (rows: queries; column: this lane's key)
-    rows_product<D, BF16, NB>(gt, koff, vf, dp);  // dP = dO V^T
+    if constexpr (V_LDS) rows_product_lds<D, BF16>(gt, koff, vres, wave, dp[0]);  // dP = dO V^T
+    else rows_product<D, BF16, NB>(gt, koff, vf, dp);
     const bool mask = (q0 + TQ > n) || (CAUSAL && q0 < kw + 31);
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb)
@@ -295,14 +334,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void bwd_dkdv_kernel(
   issue(qt0, gt0, ld0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int s = 0; s < total; s += 2) {
-    if (s + 1 < total) issue(qt1, gt1, ld1, s + 1);
-    compute(qt0, gt0, ld0, s);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (s + 1 >= total) break;
-    if (s + 2 < total) issue(qt0, gt0, ld0, s + 2);
-    compute(qt1, gt1, ld1, s + 1);
+  // one body for both stages (a second inlined copy of compute costs registers at d = 128)
+  for (int s = 0; s < total; ++s) {
+    const bool odd = s & 1;
+    if (s + 1 < total) issue(odd ? qt0 : qt1, odd ? gt0 : gt1, odd ? ld0 : ld1, s + 1);
+    compute(odd ? qt1 : qt0, odd ? gt1 : gt0, odd ? ld1 : ld0, s);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
@@ -372,7 +408,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void bwd_dq_kernel(
   operand_offsets<D>(lane, koff, vtoff);
 
   const int rowbytes = Hkv * D * 2;
-  const int voff = copy_offset<D, kTile>(wave, lane, rowbytes);
+  const int voff = copy_offset<D, kTile, kWaves>(wave, lane, rowbytes);
   const int blk_bytes = 16 * rowbytes;
   const char* kbase = reinterpret_cast<const char*>(k) + ((int64_t)seq_start * Hkv + g) * D * 2;
   const char* vbase = reinterpret_cast<const char*>(v) + ((int64_t)seq_start * Hkv + g) * D * 2;
@@ -432,8 +468,8 @@ __global__ __launch_bounds__(64 * kWaves, 2) void bwd_dq_kernel(
 
 template <int D, bool BF16, bool CAUSAL, bool VARLEN>
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
-  const int nblk = (a.N + kBlk - 1) / kBlk;
-  const long long grid_kv = (long long)nblk * a.Hkv * a.B, grid_q = (long long)nblk * a.Hq * a.B;
+  const int nblk = (a.N + kBlk - 1) / kBlk, nkv = (a.N + kKvBlk - 1) / kKvBlk;
+  const long long grid_kv = (long long)nkv * a.Hkv * a.B, grid_q = (long long)nblk * a.Hq * a.B;
   if (grid_q > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   // delta: one row per (token, query head); the grid covers the B * N tokens packed input can hold
   const int64_t blocks = ((int64_t)a.B * a.N * a.Hq * (D / 8) + 255) / 256;
@@ -443,11 +479,11 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
                      a.B, a.cu_seqlens);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16, CAUSAL, VARLEN>), dim3((unsigned)grid_kv), dim3(64 * kWaves), 0, stream,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16, CAUSAL, VARLEN>), dim3((unsigned)grid_kv), dim3(64 * kKvWaves), 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), a.lse, a.workspace,
                      static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), a.Hq, a.Hkv, a.N, a.cu_seqlens, a.B,
-                     a.alpha, nblk);
+                     a.alpha, nkv);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((bwd_dq_kernel<D, BF16, CAUSAL, VARLEN>), dim3((unsigned)grid_q), dim3(64 * kWaves), 0, stream,
