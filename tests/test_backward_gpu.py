@@ -89,7 +89,8 @@ def test_bwd_fp16():
 
 @pytest.mark.parametrize("causal", [True, False])
 def test_bwd_varlen(causal):
-    inp = si.varlen_inputs([1, 63, 64, 65, 200, 129, 300], 8, 2, 128, causal=causal, seed=804)
+    """Packed sequences of 0 .. 300 tokens (an empty one included), GQA 8:2."""
+    inp = si.varlen_inputs([1, 63, 0, 64, 65, 200, 129, 300], 8, 2, 128, causal=causal, seed=804)
     do = si.output_gradient(inp, 805)
     gu.say("bwd packed", causal)
     check_grads(inp, do, run_gpu_bwd(inp, do), f"bwd packed causal={causal}")

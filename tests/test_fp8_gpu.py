@@ -352,3 +352,16 @@ def test_fp8_attention_after_rope():
                                              .astype(np.float32)) for n in "qk"), inp.v, "bf16",
                         inp.B, inp.N, inp.Hq, inp.Hkv, inp.d, True, None, inp.seed)
     check_fp8(*_three_errors(ref, o, lse, prep, *_all_rows(ref)))
+
+
+def test_fp8_varlen_empty_sequences():
+    """Zero-length sequences in the pack: the pre-pass writes no codes or scales for them (the
+    scale entries are not defined) and attention writes no rows."""
+    inp = si.varlen_inputs([0, 70, 0, 129, 0], 4, 2, 128, causal=True, seed=623)
+    signs = si.hadamard_signs(128, seed=55)
+    gu.say("fp8 packed with empty sequences")
+    _assert_prepare_equal(gpu_prepare(inp, signs), oracle_prepare(inp, signs), "packed prepare, empty sequences")
+    _assert_prepare_equal(gpu_prepare(inp, signs, True), oracle_prepare(inp, signs, True),
+                          "packed per-tensor prepare, empty sequences")
+    o, lse, prep = gpu_fp8_attention(inp, signs)
+    check_fp8(*_three_errors(inp, o, lse, prep, *_all_rows(inp)))

@@ -77,6 +77,14 @@ def test_varlen_max_seqlen_above_longest():
     _compare_full(inp, "varlen with slack max_seqlen")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_empty_sequences(causal):
+    """Zero-length sequences anywhere in the pack (first, middle, last) write nothing and leave
+    their neighbours' rows exact."""
+    inp = si.varlen_inputs([0, 5, 0, 130, 0], 4, 2, 128, causal=causal, seed=302)
+    _compare_full(inp, f"varlen with empty sequences causal={causal}")
+
+
 def test_single_token_sequence():
     inp = si.dense_inputs(3, 1, 2, 128, causal=False, seed=301)
     _compare_full(inp, "N=1")
