@@ -9,7 +9,8 @@ Entry points carry the names of the C ABI:
 * :func:`attn_fwd` -- O and LSE of exact attention (bf16 / fp16 / fp8-e4m3 inputs; dense or
   packed variable-length; causal or not; grouped-query heads).
 * :func:`attn_fwd_window` -- the same, causal, inside a sliding window of W keys.
-* :func:`attn_bwd` -- dQ, dK, dV of attn_fwd's output (16-bit inputs).
+* :func:`attn_bwd` -- dQ, dK, dV of attn_fwd's output (16-bit inputs); with ``window`` it calls
+  ``attn_bwd_window`` (the C entry point of the same name).
 * :func:`attn_fp8_prepare` -- Hadamard rotation + per-block power-of-two e4m3 quantisation.
 * :func:`attn_fp8_prepare_ex` -- the same for packed sequences too, with per-block or per-tensor
   scales.
@@ -25,7 +26,7 @@ import re
 
 import torch
 
-__all__ = ["AttnError", "attn_fwd", "attn_fwd_window", "attn_bwd", "attention_backward", "attn_fp8_prepare", "attn_fp8_prepare_ex", "attn_strerror", "attention",
+__all__ = ["AttnError", "attn_fwd", "attn_fwd_window", "attn_bwd", "attn_bwd_window", "attention_backward", "attn_fp8_prepare", "attn_fp8_prepare_ex", "attn_strerror", "attention",
            "fp8_prepare", "load_library", "LIB_PATH", "ATTN_BF16", "ATTN_FP16", "ATTN_FP8_E4M3",
            "ATTN_FP8_SCALE_BLOCK", "ATTN_FP8_SCALE_TENSOR"]
 
@@ -65,6 +66,8 @@ def load_library(build_if_missing: bool = True):
     lib.attn_fwd_window.restype = I
     lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, P, I, I, F, I, P]
     lib.attn_bwd.restype = I
+    lib.attn_bwd_window.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, P, I, I, F, I, P]
+    lib.attn_bwd_window.restype = I
     lib.attn_bwd_workspace_bytes.argtypes = [I, I, I]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_fp8_prepare.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, P]
@@ -235,10 +238,11 @@ def attention(q, k, v, *, causal: bool = False, alpha: float | None = None, cu_s
 
 
 def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, *, causal: bool = False, alpha: float | None = None,
-             cu_seqlens=None, max_seqlen: int | None = None, stream=None) -> None:
+             cu_seqlens=None, max_seqlen: int | None = None, window: int | None = None, stream=None) -> None:
     """Enqueue attn_bwd: dq, dk, dv (q's, k's, v's layouts and dtype) of the attn_fwd call that
     produced o and lse, for the output gradient dout.  ``workspace``: float32 on the GPU with at
-    least B * Hq * N elements (it receives D = rowsum(dout * o))."""
+    least B * Hq * N elements (it receives D = rowsum(dout * o)).  With ``window``,
+    attn_bwd_window (the causal sliding window of attn_fwd_window)."""
     dev, head, tail = _fwd_call(q, k, v, o, lse, cu_seqlens, max_seqlen, None, None, None, alpha)
     for name, t, ref in (("dout", dout, o), ("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
         _check_tensor(t, name)
@@ -252,15 +256,18 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, *, causal: bool = Fal
     lib = load_library()
     alpha_v, dt = tail[0], tail[1]
     with torch.cuda.device(dev):
-        st = lib.attn_bwd(head[0], head[1], head[2], head[3], head[4], _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
-                          _ptr(workspace), B, Hq, head[7], N, head[9], head[10], int(bool(causal)), alpha_v, dt,
-                          _stream_handle(stream, dev))
+        args = (head[0], head[1], head[2], head[3], head[4], _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                _ptr(workspace), B, Hq, head[7], N, head[9], head[10])
+        if window is not None:
+            st = lib.attn_bwd_window(*args, int(window), alpha_v, dt, _stream_handle(stream, dev))
+        else:
+            st = lib.attn_bwd(*args, int(bool(causal)), alpha_v, dt, _stream_handle(stream, dev))
     if st != ATTN_OK:
-        raise AttnError(st, "attn_bwd")
+        raise AttnError(st, "attn_bwd_window" if window is not None else "attn_bwd")
 
 
 def attention_backward(q, k, v, o, lse, dout, *, causal: bool = False, alpha: float | None = None, cu_seqlens=None,
-                       max_seqlen: int | None = None, stream=None):
+                       max_seqlen: int | None = None, window: int | None = None, stream=None):
     """Allocate dq, dk, dv and the workspace and call :func:`attn_bwd`."""
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     if cu_seqlens is None:
@@ -269,7 +276,7 @@ def attention_backward(q, k, v, o, lse, dout, *, causal: bool = False, alpha: fl
         B, N, Hq = cu_seqlens.numel() - 1, int(max_seqlen), q.shape[1]
     ws = torch.empty(B * Hq * N, dtype=torch.float32, device=q.device)
     attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, causal=causal, alpha=alpha, cu_seqlens=cu_seqlens,
-             max_seqlen=max_seqlen, stream=stream)
+             max_seqlen=max_seqlen, window=window, stream=stream)
     return dq, dk, dv
 
 

@@ -62,6 +62,26 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   return status_of(err);
 }
 
+// attn_bwd and attn_bwd_window: window = 0 is no window.
+int bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+        void* dk, void* dv, float* workspace, int B, int Hq, int Hkv, int N, const int* cu_seqlens, int d, int causal,
+        int window, float alpha, attn_dtype_t dtype, hipStream_t stream) {
+  int rc = validate_common(q, k, v, o, lse, B, Hq, Hkv, N);
+  if (rc != ATTN_OK) return rc;
+  if (!dout || !dq || !dk || !dv || !workspace) return ATTN_ERR_INVALID;
+  if (!(isfinite(alpha) && alpha > 0.f)) return ATTN_ERR_INVALID;
+  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  // the kernels address one head's Q (and dO) rows with 32-bit byte offsets
+  if ((long long)N * Hq * d * 2 > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
+    return ATTN_ERR_ALIGN;
+  attn::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, cu_seqlens, d, causal, window, alpha};
+  return status_of(attn::launch_bwd_16bit(a, dtype == ATTN_BF16, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -102,20 +122,16 @@ size_t attn_bwd_workspace_bytes(int B, int Hq, int N) {
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
              void* dq, void* dk, void* dv, float* workspace, int B, int Hq, int Hkv, int N, const int* cu_seqlens,
              int d, int causal, float alpha, attn_dtype_t dtype, hipStream_t stream) {
-  int rc = validate_common(q, k, v, o, lse, B, Hq, Hkv, N);
-  if (rc != ATTN_OK) return rc;
-  if (!dout || !dq || !dk || !dv || !workspace) return ATTN_ERR_INVALID;
-  if (!(isfinite(alpha) && alpha > 0.f)) return ATTN_ERR_INVALID;
-  if (causal != 0 && causal != 1) return ATTN_ERR_INVALID;
-  if (dtype != ATTN_BF16 && dtype != ATTN_FP16) return ATTN_ERR_UNSUPPORTED;
-  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
-  // the kernels address one head's Q (and dO) rows with 32-bit byte offsets
-  if ((long long)N * Hq * d * 2 > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
-      !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
-    return ATTN_ERR_ALIGN;
-  attn::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, cu_seqlens, d, causal, alpha};
-  return status_of(attn::launch_bwd_16bit(a, dtype == ATTN_BF16, stream));
+  return bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, cu_seqlens, d, causal, 0, alpha, dtype,
+             stream);
+}
+
+int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                    void* dq, void* dk, void* dv, float* workspace, int B, int Hq, int Hkv, int N,
+                    const int* cu_seqlens, int d, int window, float alpha, attn_dtype_t dtype, hipStream_t stream) {
+  if (window < 1) return ATTN_ERR_INVALID;
+  return bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, cu_seqlens, d, 1, window < N ? window : 0,
+             alpha, dtype, stream);
 }
 
 int attn_fp8_prepare(const void* q, const void* k, const void* v, void* q8, void* k8, void* v8,

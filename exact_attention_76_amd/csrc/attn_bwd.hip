@@ -185,12 +185,14 @@ __device__ __forceinline__ int copy_offset(int wave, int lane, int rowbytes) {
 }
 
 // ---- dK, dV -------------------------------------------------------------------------------------
-template <int D, bool BF16, bool CAUSAL, bool VARLEN>
+// WINDOW (implies CAUSAL): causal sliding window of `window` keys (query i sees keys
+// i-window+1 .. i); otherwise `window` is unused.
+template <int D, bool BF16, bool CAUSAL, bool VARLEN, bool WINDOW>
 __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int Hq, int Hkv, int N, const int* __restrict__ cu_seqlens,
-    int nseq, float alpha, int num_kblocks) {
+    int nseq, float alpha, int num_kblocks, int window) {
   constexpr int NCH = D / 8, KS_D = D / 16, NB_D = D / 32;
   constexpr int TQ = dkdv_tile<D>();  // queries per tile
   constexpr int TILE = TQ * D * 2;
@@ -263,9 +265,11 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(
   const int voff = copy_offset<D, TQ, kKvWaves>(wave, lane, rowbytes);
   const int blk_bytes = 16 * rowbytes;
   const int nbytes = (n - 1) * rowbytes + D * 2;
-  // causal: the first query tile that holds a query >= the block's first key
+  // causal: the first query tile that holds a query >= the block's first key; window: the last
+  // one holds the last query that sees the block's last key
   const int t_first = CAUSAL ? k0 / TQ : 0;
-  const int ntiles = (n + TQ - 1) / TQ - t_first;
+  const int q_end = WINDOW ? min(n, k0 + kKvBlk - 1 + window) : n;
+  const int ntiles = (q_end + TQ - 1) / TQ - t_first;
   const int total = G * ntiles;  // (head, tile) steps
   const int64_t lstride = VARLEN ? (int64_t)cu_seqlens[nseq] : (int64_t)N;
 
@@ -299,11 +303,12 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(
   auto compute = [&](const char* qt, const char* gt, float (*ldt)[256], int s) {
     const int q0 = (t_first + s % ntiles) * TQ;
     if (CAUSAL && q0 + TQ - 1 < kw) return;  // every query of the tile is before this wave's keys
+    if (WINDOW && q0 > kw + 31 + window - 1) return;  // every query is past this wave's windows
     f32x16 sc[NB], dp[NB];
     rows_product<D, BF16, NB>(qt, koff, kf, sc);  // S = Q K^T (rows: queries; column: this lane's key)
     if constexpr (V_LDS) rows_product_lds<D, BF16>(gt, koff, vres, wave, dp[0]);  // dP = dO V^T
     else rows_product<D, BF16, NB>(gt, koff, vf, dp);
-    const bool mask = (q0 + TQ > n) || (CAUSAL && q0 < kw + 31);
+    const bool mask = (q0 + TQ > n) || (CAUSAL && q0 < kw + 31) || (WINDOW && q0 + TQ - 1 > kw + window - 1);
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb)
 #pragma unroll
@@ -318,7 +323,11 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(
           float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cb][r], c, -Lr[e] * kLog2e));
           if (mask) {
             const int qi = q0 + row0 + e;
-            if (qi >= n || (CAUSAL && qi < kj)) p = 0.f;
+            if constexpr (WINDOW) {  // visible iff 0 <= qi - kj < window
+              if (qi >= n || (unsigned)(qi - kj) >= (unsigned)window) p = 0.f;
+            } else {
+              if (qi >= n || (CAUSAL && qi < kj)) p = 0.f;
+            }
           }
           sc[cb][r] = p;
           dp[cb][r] = p * (dp[cb][r] - Dr[e]);
@@ -351,12 +360,12 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(
 }
 
 // ---- dQ -----------------------------------------------------------------------------------------
-template <int D, bool BF16, bool CAUSAL, bool VARLEN>
+template <int D, bool BF16, bool CAUSAL, bool VARLEN, bool WINDOW>
 __global__ __launch_bounds__(64 * kWaves, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, const float* __restrict__ delta,
     uint16_t* __restrict__ dq, int Hq, int Hkv, int N, const int* __restrict__ cu_seqlens, int nseq, float alpha,
-    int num_qblocks) {
+    int num_qblocks, int window) {
   constexpr int NCH = D / 8, KS_D = D / 16, NB_D = D / 32;
   constexpr int TILE = kTile * D * 2;
   constexpr int NI = TILE / 1024 / kWaves, IPB = NCH / 4;
@@ -413,13 +422,15 @@ __global__ __launch_bounds__(64 * kWaves, 2) void bwd_dq_kernel(
   const char* kbase = reinterpret_cast<const char*>(k) + ((int64_t)seq_start * Hkv + g) * D * 2;
   const char* vbase = reinterpret_cast<const char*>(v) + ((int64_t)seq_start * Hkv + g) * D * 2;
   const int nbytes = (n - 1) * rowbytes + D * 2;
-  auto issue = [&](char* kdst, char* vdst, int tile) {
-    const int off = tile * kTile * rowbytes;
+  const int kv_end = CAUSAL ? min(n, q0 + kBlk) : n;
+  // window: the loop counts key tiles from t0, the first one the block's first query sees
+  const int t0 = WINDOW ? max(0, q0 - window + 1) / kTile : 0;
+  const int ntiles = (kv_end + kTile - 1) / kTile - t0;
+  auto issue = [&](char* kdst, char* vdst, int j) {
+    const int off = (t0 + j) * kTile * rowbytes;
     copy_rows_to_lds<NI, IPB>(kbase + off, nbytes - off, kdst + wave * NI * 1024, voff, blk_bytes);
     copy_rows_to_lds<NI, IPB>(vbase + off, nbytes - off, vdst + wave * NI * 1024, voff, blk_bytes);
   };
-  const int kv_end = CAUSAL ? min(n, q0 + kBlk) : n;
-  const int ntiles = (kv_end + kTile - 1) / kTile;
 
   f32x16 dqa[NB_D];
 #pragma unroll
@@ -427,12 +438,13 @@ __global__ __launch_bounds__(64 * kWaves, 2) void bwd_dq_kernel(
   const float c = alpha * kLog2e;
 
   auto compute = [&](const char* kt, const char* vt, int j) {
-    const int j0 = j * kTile;
+    const int j0 = (t0 + j) * kTile;
     if (CAUSAL && j0 > qw + 31) return;  // the tile lies wholly after this wave's queries
+    if (WINDOW && j0 + kTile - 1 <= qw - window) return;  // wholly before this wave's windows
     f32x16 sc[NB], dp[NB];
     rows_product<D, BF16, NB>(kt, koff, qf, sc);  // S^T = K Q^T (rows: keys; column: this lane's query)
     rows_product<D, BF16, NB>(vt, koff, gf, dp);  // dP^T = V dO^T
-    const bool mask = (j0 + kTile > n) || (CAUSAL && j0 + kTile - 1 > qw);
+    const bool mask = (j0 + kTile > n) || (CAUSAL && j0 + kTile - 1 > qw) || (WINDOW && j0 <= qw + 31 - window);
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb)
 #pragma unroll
@@ -440,7 +452,11 @@ __global__ __launch_bounds__(64 * kWaves, 2) void bwd_dq_kernel(
         float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cb][r], c, -Lc));
         if (mask) {
           const int key = j0 + 32 * cb + acc_row(r, hi);
-          if (key >= n || (CAUSAL && key > qi)) p = 0.f;
+          if constexpr (WINDOW) {  // visible iff 0 <= qi - key < window
+            if (key >= n || (unsigned)(qi - key) >= (unsigned)window) p = 0.f;
+          } else {
+            if (key >= n || (CAUSAL && key > qi)) p = 0.f;
+          }
         }
         dp[cb][r] = p * (dp[cb][r] - Dq);
       }
@@ -466,7 +482,7 @@ __global__ __launch_bounds__(64 * kWaves, 2) void bwd_dq_kernel(
   if (qi < n) store_rows<D, BF16>(dq + ((int64_t)(seq_start + qi) * Hq + h) * D, dqa, alpha, hi);
 }
 
-template <int D, bool BF16, bool CAUSAL, bool VARLEN>
+template <int D, bool BF16, bool CAUSAL, bool VARLEN, bool WINDOW = false>
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   const int nblk = (a.N + kBlk - 1) / kBlk, nkv = (a.N + kKvBlk - 1) / kKvBlk;
   const long long grid_kv = (long long)nkv * a.Hkv * a.B, grid_q = (long long)nblk * a.Hq * a.B;
@@ -479,23 +495,26 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
                      a.B, a.cu_seqlens);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16, CAUSAL, VARLEN>), dim3((unsigned)grid_kv), dim3(64 * kKvWaves), 0, stream,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, BF16, CAUSAL, VARLEN, WINDOW>), dim3((unsigned)grid_kv), dim3(64 * kKvWaves), 0,
+                     stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), a.lse, a.workspace,
                      static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), a.Hq, a.Hkv, a.N, a.cu_seqlens, a.B,
-                     a.alpha, nkv);
+                     a.alpha, nkv, a.window);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, BF16, CAUSAL, VARLEN>), dim3((unsigned)grid_q), dim3(64 * kWaves), 0, stream,
+  hipLaunchKernelGGL((bwd_dq_kernel<D, BF16, CAUSAL, VARLEN, WINDOW>), dim3((unsigned)grid_q), dim3(64 * kWaves), 0, stream,
                      static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.dout), a.lse, a.workspace,
-                     static_cast<uint16_t*>(a.dq), a.Hq, a.Hkv, a.N, a.cu_seqlens, a.B, a.alpha, nblk);
+                     static_cast<uint16_t*>(a.dq), a.Hq, a.Hkv, a.N, a.cu_seqlens, a.B, a.alpha, nblk, a.window);
   return hipGetLastError();
 }
 
 template <int D, bool BF16>
 hipError_t launch_bwd_modes(const BwdArgs& a, hipStream_t stream) {
   const bool varlen = a.cu_seqlens != nullptr;
+  if (a.window > 0)
+    return varlen ? launch_bwd<D, BF16, true, true, true>(a, stream) : launch_bwd<D, BF16, true, false, true>(a, stream);
   if (a.causal) return varlen ? launch_bwd<D, BF16, true, true>(a, stream) : launch_bwd<D, BF16, true, false>(a, stream);
   return varlen ? launch_bwd<D, BF16, false, true>(a, stream) : launch_bwd<D, BF16, false, false>(a, stream);
 }

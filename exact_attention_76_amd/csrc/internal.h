@@ -45,6 +45,7 @@ struct BwdArgs {
   const int* cu_seqlens;      // device int32 [B+1] or nullptr
   int d;
   int causal;
+  int window;                 // causal sliding window of this many keys, or 0 for none
   float alpha;
 };
 

@@ -136,6 +136,17 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              int B, int Hq, int Hkv, int N, const int* cu_seqlens,
              int d, int causal, float alpha, attn_dtype_t dtype, hipStream_t stream);
 
+/*
+ * attn_bwd_window -- attn_bwd for attn_fwd_window's output: causal attention inside a
+ * sliding window of `window` keys (query i sees keys i-window+1 .. i; window >= 1, else
+ * ATTN_ERR_INVALID; window >= N is plain causal).  Arguments otherwise as attn_bwd with
+ * causal = 1.
+ */
+int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                    const void* dout, void* dq, void* dk, void* dv, float* workspace,
+                    int B, int Hq, int Hkv, int N, const int* cu_seqlens,
+                    int d, int window, float alpha, attn_dtype_t dtype, hipStream_t stream);
+
 /* Bytes of workspace attn_bwd needs (B * Hq * N floats); 0 for non-positive sizes. */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int N);
 

@@ -19,7 +19,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = ea.header_functions()
-    assert set(names) == {"attn_fwd", "attn_fwd_window", "attn_bwd", "attn_bwd_workspace_bytes", "attn_fp8_prepare",
+    assert set(names) == {"attn_fwd", "attn_fwd_window", "attn_bwd", "attn_bwd_window", "attn_bwd_workspace_bytes",
+                          "attn_fp8_prepare",
                           "attn_fp8_prepare_ex", "attn_strerror"}
     out = subprocess.run(["nm", "-D", "--defined-only", ea.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
@@ -179,3 +180,10 @@ def test_bwd_validation(lib, kw, status):
 def test_bwd_workspace_bytes(lib):
     assert lib.attn_bwd_workspace_bytes(2, 16, 8192) == 2 * 16 * 8192 * 4
     assert lib.attn_bwd_workspace_bytes(0, 16, 8192) == 0
+
+
+@pytest.mark.parametrize("window,status", [(0, ea.ATTN_ERR_INVALID), (-1, ea.ATTN_ERR_INVALID)])
+def test_bwd_window_validation(lib, window, status):
+    P = ctypes.c_void_p
+    assert lib.attn_bwd_window(P(A), P(A), P(A), P(A), P(A), P(A), P(A), P(A), P(A), P(A), 1, 2, 2, 128, None, 128,
+                               window, 0.125, ea.ATTN_BF16, None) == status

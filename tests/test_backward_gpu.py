@@ -34,7 +34,8 @@ def run_gpu_bwd(inp, do_bits):
 
     q, k, v, cu = gu.to_device(inp)
     do = torch.from_numpy(do_bits.view(np.int16)).view(gu.torch_dtype(inp.dtype)).cuda()
-    kw = dict(causal=inp.causal, alpha=inp.alpha, cu_seqlens=cu, max_seqlen=inp.N if cu is not None else None)
+    kw = dict(causal=inp.causal, alpha=inp.alpha, cu_seqlens=cu, max_seqlen=inp.N if cu is not None else None,
+              window=inp.window or None)
     o, lse = ea.attention(q, k, v, **kw)
     dq, dk, dv = ea.attention_backward(q, k, v, o, lse, do, **kw)
     torch.cuda.synchronize()
@@ -54,7 +55,7 @@ def check_grads(inp, do_bits, got, what, heads=None):
         sel_k = (slice(None), slice(None), np.asarray(heads)) if dense else (slice(None), np.asarray(heads))
         q, do, k, v = q[sel_q], do[sel_q], k[sel_k], v[sel_k]
         got = (got[0][sel_q], got[1][sel_k], got[2][sel_k])
-    kw = dict(causal=inp.causal, alpha=inp.alpha, cu_seqlens=inp.cu_seqlens)
+    kw = dict(causal=inp.causal, alpha=inp.alpha, cu_seqlens=inp.cu_seqlens, window=inp.window)
     ref = ob.attention_backward(q, k, v, do, **kw)
     u = 2.0 ** -SIG_BITS[inp.dtype]
     o_ref, _ = oracle.attention(q, k, v, **kw)
@@ -112,3 +113,23 @@ def test_bwd_full_gqa_packed():
     do = si.output_gradient(inp, 808)
     gu.say("bwd full packed GQA")
     check_grads(inp, do, run_gpu_bwd(inp, do), "bwd full packed GQA", heads=[5])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("window", [1, 33, 100, 300, 1000])
+def test_bwd_window(d, window):
+    """Sliding windows below, at and past the tile sizes (64 keys, 32 or 64 queries, 128 and 256
+    rows per workgroup) and past the sequence (plain causal)."""
+    inp = si.dense_inputs(2, 700, 4, d, Hkv=2, causal=True, seed=809 + d)
+    inp.window = window
+    do = si.output_gradient(inp, 810)
+    gu.say("bwd window", d, window)
+    check_grads(inp, do, run_gpu_bwd(inp, do), f"bwd window {window} d={d}")
+
+
+def test_bwd_window_packed():
+    inp = si.varlen_inputs([1, 63, 0, 300, 129, 520], 8, 2, 128, causal=True, seed=811)
+    inp.window = 77
+    do = si.output_gradient(inp, 812)
+    gu.say("bwd window packed")
+    check_grads(inp, do, run_gpu_bwd(inp, do), "bwd window packed")
