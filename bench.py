@@ -56,13 +56,15 @@ HBM_PEAK_GBS = 8000.0
 # only for the kernel sources it was taken on (sha256 prefix of each file); any other version
 # reports null.
 _DEC = "exact_attention_76_amd/csrc/decompose.h"
+_T16 = "exact_attention_76_amd/csrc/tile16.h"
 MEASURED_TRAFFIC = {
-    "bf16_mha16k": {"sources": {"exact_attention_76_amd/csrc/attn_fwd.hip": "9db5dce1e60553b2",
-                                _DEC: "5177b80538cd69cc"}, "bytes": 404032918},
-    "fp8_attention": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "c53af65c5945ed85",
-                                  _DEC: "5177b80538cd69cc"}, "bytes": 185699483},
-    "fp8_prepare": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "c53af65c5945ed85"},
-                    "bytes": 302673101},
+    "bf16_mha16k": {"sources": {"exact_attention_76_amd/csrc/attn_fwd.hip": "549c7fde5c869bf2",
+                                _DEC: "5177b80538cd69cc", _T16: "91339639cbec1225"},
+                    "bytes": 404107641},
+    "fp8_attention": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "4850044002955a22",
+                                  _DEC: "5177b80538cd69cc"}, "bytes": 185688482},
+    "fp8_prepare": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "4850044002955a22"},
+                    "bytes": 302670970},
 }
 
 
