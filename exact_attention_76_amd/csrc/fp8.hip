@@ -393,7 +393,19 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 3 : 1)) void fwd_fp8_kern
   const char* kbase = reinterpret_cast<const char*>(k) + ((int64_t)seq_start * Hkv + g) * kD;
   const char* vbase = reinterpret_cast<const char*>(v) + ((int64_t)seq_start * Hkv + g) * kD;
   const int nbytes = (n - 1) * rowbytes + kD;
-  auto issue_tile = [&](char* stage, int tile) {
+  // Raw K and V scales of one tile (one per 64-key block).  A tile's scales are loaded just
+  // before its copies are issued and read only after the wait that ends the previous tile, so
+  // no wait on a scale load also waits for a tile copy still in flight.
+  struct TileScales {
+    float k[KS], v[KS];
+  };
+  auto issue_tile = [&](char* stage, int tile, TileScales& sc) {
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      const int blk = min(tile * (BC / 64) + i, nblk - 1);
+      sc.k[i] = ksc[blk];
+      sc.v[i] = vsc[blk];
+    }
     const int off = tile * BC * rowbytes;
     copy_rows_to_lds8<NI>(kbase + off, nbytes - off, stage + wave * NI * 1024, voff);
     copy_rows_to_lds8<NI>(vbase + off, nbytes - off, stage + TILE + wave * NI * 1024, voff);
@@ -428,14 +440,14 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 3 : 1)) void fwd_fp8_kern
     return !CAUSAL || (k0 <= qw + 31 && (!WINDOW || k0 + BC - 1 > qw - window));
   };
 
-  auto compute_tile = [&](const char* stage, int j) {
+  auto compute_tile = [&](const char* stage, int j, const TileScales& sc) {
     const char* kt = stage;
     const char* vt = stage + TILE;
     const int k0 = (t0 + j) * BC;
     f32x16 s[NB_C];
 #pragma unroll
     for (int cb = 0; cb < NB_C; ++cb) {
-      const int sk = e8m0_of(ksc[(k0 >> 6) + (cb >> 1)]);
+      const int sk = e8m0_of(sc.k[cb >> 1]);
       s[cb] = f32x16{};
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -499,7 +511,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 3 : 1)) void fwd_fp8_kern
         const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(s[cb][r0], s[cb][r0 + 1], __float_as_int(s[cb][r0]), false);
         pf[w] = __builtin_amdgcn_cvt_pk_fp8_f32(s[cb][r0 + 2], s[cb][r0 + 3], lo, true);
       }
-      const int sv = e8m0_of(vsc[(k0 >> 6) + kk]);
+      const int sv = e8m0_of(sc.v[kk]);
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         i32x8 a;
@@ -515,20 +527,25 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 3 : 1)) void fwd_fp8_kern
     }
   };
 
-  issue_tile(st0, t0);
+  // The Q fragment must have arrived before the loop: loads still in flight at its entry would
+  // make every iteration wait for all vector memory operations, the tile copies included.
+  asm volatile("" ::"v"(qf[0]), "v"(qf[1]));
+  TileScales sc0, sc1;  // scales of the tiles in st0 and st1
+  issue_tile(st0, t0, sc0);
+  sc1 = sc0;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   // causal: a wave skips the tiles that lie wholly above its diagonal or before its window; it
   // still copies and waits.  A lane whose keys in a tile are all masked keeps m = -inf and adds
   // nothing (P = exp2(-inf) = 0).
   for (int j = 0; j < ntiles; j += 2) {
-    if (j + 1 < ntiles) issue_tile(st1, t0 + j + 1);
-    if (wave_needs(j)) compute_tile(st0, j);
+    if (j + 1 < ntiles) issue_tile(st1, t0 + j + 1, sc1);
+    if (wave_needs(j)) compute_tile(st0, j, sc0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (j + 1 >= ntiles) break;
-    if (j + 2 < ntiles) issue_tile(st0, t0 + j + 2);
-    if (wave_needs(j + 1)) compute_tile(st1, j + 1);
+    if (j + 2 < ntiles) issue_tile(st0, t0 + j + 2, sc0);
+    if (wave_needs(j + 1)) compute_tile(st1, j + 1, sc1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
