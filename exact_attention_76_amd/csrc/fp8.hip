@@ -27,7 +27,7 @@
 //     share here, and three waves per SIMD hide it better than two in a ping-pong -- and both
 //     products on v_mfma_scale_f32_32x32x64_f8f6f4.  The per-block power-of-two scales of
 //     Q, K and V go into the instruction's E8M0 scale operands, so they cost nothing.  P is
-//     quantised as e4m3 of 2^8 * P (the 2^8 rides in the exp2 argument and cancels against the
+//     quantised as e4m3 of 2^6 * P (the 2^6 rides in the exp2 argument and cancels against the
 //     row sum, which is summed from the unquantised values).  V is read transposed from LDS
 //     with ds_read_b64_tr_b8, the key order matching the byte order of the P operand.
 #include <hip/hip_runtime.h>
@@ -324,12 +324,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// P is quantised as e4m3(2^kPExp * P); with a row maximum at most kRescaleSlack (exp2 domain)
+// above the stabiliser, 2^kPExp * P <= 2^(kPExp + kRescaleSlack) <= 448.
+constexpr int kPExp = 6;
+constexpr float kRescaleSlack = 2.75f;
+static_assert(kPExp + kRescaleSlack <= 8.807f, "2^(kPExp + kRescaleSlack) must not exceed 448 = 2^8.807");
+
 // WAVES waves of 32 queries per workgroup; BC keys per tile (64 or 128, a multiple of the
 // 64-token scale block).  CAUSAL: key j visible to query i iff j <= i.  VARLEN: packed sequences
 // [T, H, d] delimited by cu_seqlens, scale blocks counted from each sequence's first token.
 // WINDOW (implies CAUSAL): query i sees keys i-window+1 .. i only.
-template <int WAVES, int BC, bool CAUSAL, bool VARLEN, bool WINDOW>
-__global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 3 : 1)) void fwd_fp8_kernel(
+// PIPE: two-stage loop (three K/V buffers, two waves per SIMD): each wave issues the first
+// product of tile j+1 before the softmax of tile j, so the matrix core works on the next tile
+// while the vector ALUs take the exponentials of this one.  Otherwise one stage per tile (two
+// buffers, three waves per SIMD).
+template <int WAVES, int BC, bool PIPE, bool CAUSAL, bool VARLEN, bool WINDOW>
+__global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? (PIPE ? 2 : 3) : 1)) void fwd_fp8_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
     const float* __restrict__ qs, const float* __restrict__ ks_, const float* __restrict__ vs_,
     uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int N, const int* __restrict__ cu_seqlens,
@@ -342,6 +352,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 3 : 1)) void fwd_fp8_kern
   static_assert(BC % 64 == 0 && NI >= 1 && NI * WAVES * 1024 == TILE, "tile shape");
   __shared__ __attribute__((aligned(1024))) char st0[2 * TILE];
   __shared__ __attribute__((aligned(1024))) char st1[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) char st2[PIPE ? 2 * TILE : 1];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -440,11 +451,9 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 3 : 1)) void fwd_fp8_kern
     return !CAUSAL || (k0 <= qw + 31 && (!WINDOW || k0 + BC - 1 > qw - window));
   };
 
-  auto compute_tile = [&](const char* stage, int j, const TileScales& sc) {
+  // first product of loop tile j: S^T = K Q^T from the K half of its buffer
+  auto gemm1 = [&](const char* stage, const TileScales& sc, f32x16* s) {
     const char* kt = stage;
-    const char* vt = stage + TILE;
-    const int k0 = (t0 + j) * BC;
-    f32x16 s[NB_C];
 #pragma unroll
     for (int cb = 0; cb < NB_C; ++cb) {
       const int sk = e8m0_of(sc.k[cb >> 1]);
@@ -457,6 +466,12 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 3 : 1)) void fwd_fp8_kern
         s[cb] = mma_f8(a, qf[st], s[cb], sk, sq);
       }
     }
+  };
+  // mask, online softmax and second product of loop tile j (scores s) from the V half of its
+  // buffer
+  auto softmax_gemm2 = [&](const char* stage, int j, const TileScales& sc, f32x16* s) {
+    const char* vt = stage + TILE;
+    const int k0 = (t0 + j) * BC;
     if (k0 + BC > n || (CAUSAL && (k0 + BC - 1 > qw || (WINDOW && k0 <= qw + 31 - window)))) {
 #pragma unroll
       for (int cb = 0; cb < NB_C; ++cb)
@@ -476,9 +491,10 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 3 : 1)) void fwd_fp8_kern
 #pragma unroll
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[cb][r]);
     mt = halves_max(mt);
-    // P' = 2^8 * exp2((s - m) c) must stay below 448 (largest e4m3): rescale once some row's
-    // maximum exceeds the stabiliser by more than 0.75 in the exp2 domain.
-    const float thr = (m == -INFINITY) ? -INFINITY : m * c + 0.75f;
+    // P' = 2^kPExp * exp2((s - m) c) must stay at or below 448 (largest e4m3): rescale once some
+    // row's maximum exceeds the stabiliser by more than kRescaleSlack in the exp2 domain
+    // (2^(6 + 2.75) = 430.5).  A smaller kPExp leaves more slack, so rescales are rarer.
+    const float thr = (m == -INFINITY) ? -INFINITY : m * c + kRescaleSlack;
     if (__builtin_amdgcn_ballot_w64(mt * c > thr)) {
       const float mnew = fmaxf(m, mt);
       const float corr = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - mnew) * c);
@@ -487,7 +503,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 3 : 1)) void fwd_fp8_kern
 #pragma unroll
       for (int db = 0; db < 4; ++db) oacc[db] *= corr;
     }
-    const float mc = ((m == -INFINITY) ? 0.f : m * c) - 8.f;
+    const float mc = ((m == -INFINITY) ? 0.f : m * c) - (float)kPExp;
     float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int cb = 0; cb < NB_C; ++cb)
@@ -530,24 +546,70 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 3 : 1)) void fwd_fp8_kern
   // The Q fragment must have arrived before the loop: loads still in flight at its entry would
   // make every iteration wait for all vector memory operations, the tile copies included.
   asm volatile("" ::"v"(qf[0]), "v"(qf[1]));
-  TileScales sc0, sc1;  // scales of the tiles in st0 and st1
-  issue_tile(st0, t0, sc0);
-  sc1 = sc0;
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
   // causal: a wave skips the tiles that lie wholly above its diagonal or before its window; it
   // still copies and waits.  A lane whose keys in a tile are all masked keeps m = -inf and adds
   // nothing (P = exp2(-inf) = 0).
-  for (int j = 0; j < ntiles; j += 2) {
-    if (j + 1 < ntiles) issue_tile(st1, t0 + j + 1, sc1);
-    if (wave_needs(j)) compute_tile(st0, j, sc0);
+  if constexpr (!PIPE) {
+    TileScales sc0, sc1;  // scales of the tiles in st0 and st1
+    issue_tile(st0, t0, sc0);
+    sc1 = sc0;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (j + 1 >= ntiles) break;
-    if (j + 2 < ntiles) issue_tile(st0, t0 + j + 2, sc0);
-    if (wave_needs(j + 1)) compute_tile(st1, j + 1, sc1);
+    f32x16 s[NB_C];
+    for (int j = 0; j < ntiles; j += 2) {
+      if (j + 1 < ntiles) issue_tile(st1, t0 + j + 1, sc1);
+      if (wave_needs(j)) {
+        gemm1(st0, sc0, s);
+        softmax_gemm2(st0, j, sc0, s);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (j + 1 >= ntiles) break;
+      if (j + 2 < ntiles) issue_tile(st0, t0 + j + 2, sc0);
+      if (wave_needs(j + 1)) {
+        gemm1(st1, sc1, s);
+        softmax_gemm2(st1, j + 1, sc1, s);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  } else {
+    // Loop tile j lives in buffer j % 3.  Step j copies tile j+2 into the buffer of tile j-1
+    // (whose last reads, the second product of step j-1, ended before the barrier closing that
+    // step), forms S_{j+1} from the K half of tile j+1, then takes the softmax of S_j and the
+    // second product with the V half of tile j.  Its wait and barrier make tile j+2 visible
+    // for step j+1.  The score registers alternate between sa and sb, so the loop is unrolled
+    // six times to name every buffer and register set statically.
+    TileScales sc0, sc1, sc2;
+    issue_tile(st0, t0, sc0);
+    sc2 = sc1 = sc0;
+    if (ntiles > 1) issue_tile(st1, t0 + 1, sc1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    f32x16 sa[NB_C], sb[NB_C];
+    if (wave_needs(0)) gemm1(st0, sc0, sa);
+    auto step = [&](int j, char* cur, char* nxt, char* fut, const TileScales& scc, const TileScales& scn,
+                    TileScales& scf, f32x16* s_cur, f32x16* s_nxt) {
+      if (j + 2 < ntiles) issue_tile(fut, t0 + j + 2, scf);
+      if (j + 1 < ntiles && wave_needs(j + 1)) gemm1(nxt, scn, s_nxt);
+      if (wave_needs(j)) softmax_gemm2(cur, j, scc, s_cur);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    };
+    for (int j = 0;; j += 6) {
+      step(j, st0, st1, st2, sc0, sc1, sc2, sa, sb);
+      if (j + 1 >= ntiles) break;
+      step(j + 1, st1, st2, st0, sc1, sc2, sc0, sb, sa);
+      if (j + 2 >= ntiles) break;
+      step(j + 2, st2, st0, st1, sc2, sc0, sc1, sa, sb);
+      if (j + 3 >= ntiles) break;
+      step(j + 3, st0, st1, st2, sc0, sc1, sc2, sb, sa);
+      if (j + 4 >= ntiles) break;
+      step(j + 4, st1, st2, st0, sc1, sc2, sc0, sa, sb);
+      if (j + 5 >= ntiles) break;
+      step(j + 5, st2, st0, st1, sc2, sc0, sc1, sb, sa);
+      if (j + 6 >= ntiles) break;
+    }
   }
 
   const float lt = halves_sum(l);
@@ -563,15 +625,15 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 3 : 1)) void fwd_fp8_kern
         *reinterpret_cast<u32x2*>(op + db * 32 + gq * 8) = pr;
       }
     if (hi == 0) {
-      // l carries the factor 2^8 of P'
+      // l carries the factor 2^kPExp of P'
       const int64_t idx = VARLEN ? (int64_t)h * cu_seqlens[nseq] + seq_start + qi : ((int64_t)b * Hq + h) * N + qi;
-      lse[idx] = lt > 0.f ? m * alpha + __logf(lt) - 8.f * kLn2 : -INFINITY;
+      lse[idx] = lt > 0.f ? m * alpha + __logf(lt) - (float)kPExp * kLn2 : -INFINITY;
     }
   }
 }
 
 #ifndef ATTN_FP8_SHAPE
-#define ATTN_FP8_SHAPE 4, 64
+#define ATTN_FP8_SHAPE 4, 64, false
 #endif
 
 }  // namespace

@@ -280,8 +280,9 @@ def test_fp8_attention_varlen(causal, per_tensor):
 
 def test_fp8_attention_causal_row0_is_v0():
     """Causal row 0 sees key 0 only, so O_0 is V_0 as quantised (an e4m3 value times a power of
-    two, which bf16 holds exactly): P and l are both 2^8 up to a few fp32 ulps, P rounds to
-    exactly 2^8 in e4m3, and O_0 = V_0 (1 + O(2^-20)) rounds back to V_0.  L_0 is the score of
+    two, which bf16 holds exactly): P and l are both the kernel's power-of-two prefactor of P
+    (2^6) up to a few fp32 ulps, P rounds to exactly that power of two in e4m3, and
+    O_0 = V_0 (1 + O(2^-20)) rounds back to V_0.  L_0 is the score of
     that one key."""
     inp = si.dense_inputs(1, 256, 4, 128, causal=True, seed=613)
     gu.say("fp8 causal row 0")
