@@ -61,10 +61,10 @@ MEASURED_TRAFFIC = {
     "bf16_mha16k": {"sources": {"exact_attention_76_amd/csrc/attn_fwd.hip": "549c7fde5c869bf2",
                                 _DEC: "5177b80538cd69cc", _T16: "91339639cbec1225"},
                     "bytes": 404107641},
-    "fp8_attention": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "dfb9b1900c277cf8",
-                                  _DEC: "5177b80538cd69cc"}, "bytes": 189498573},
-    "fp8_prepare": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "dfb9b1900c277cf8"},
-                    "bytes": 302646886},
+    "fp8_attention": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "e05304fe55bd884d",
+                                  _DEC: "5177b80538cd69cc"}, "bytes": 189210020},
+    "fp8_prepare": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "e05304fe55bd884d"},
+                    "bytes": 302682812},
 }
 
 
