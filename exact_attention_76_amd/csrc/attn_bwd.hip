@@ -343,13 +343,33 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(
   issue(qt0, gt0, ld0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  // one body for both stages (a second inlined copy of compute costs registers at d = 128)
-  for (int s = 0; s < total; ++s) {
-    const bool odd = s & 1;
-    if (s + 1 < total) issue(odd ? qt0 : qt1, odd ? gt0 : gt1, odd ? ld0 : ld1, s + 1);
-    compute(odd ? qt1 : qt0, odd ? gt1 : gt0, odd ? ld1 : ld0, s);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+  // Unrolled by two, every LDS read names its buffer, and the compiler can tell it from the one
+  // the next step's copies are filling.  With one body for both stages (buffers chosen at run
+  // time) it waits for those copies before the step's first read of L.  The second inlined
+  // copy of compute fits the registers of two waves per SIMD at d = 64 and for causal d = 128
+  // (one spilled register, outside the loop); non-causal d = 128 would spill in the loop, so it
+  // keeps the single body.
+  constexpr bool UNROLL = D == 64 || CAUSAL;
+  if constexpr (UNROLL) {
+    for (int s = 0; s < total; s += 2) {
+      if (s + 1 < total) issue(qt1, gt1, ld1, s + 1);
+      compute(qt0, gt0, ld0, s);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (s + 1 >= total) break;
+      if (s + 2 < total) issue(qt0, gt0, ld0, s + 2);
+      compute(qt1, gt1, ld1, s + 1);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  } else {
+    for (int s = 0; s < total; ++s) {
+      const bool odd = s & 1;
+      if (s + 1 < total) issue(odd ? qt0 : qt1, odd ? gt0 : gt1, odd ? ld0 : ld1, s + 1);
+      compute(odd ? qt1 : qt0, odd ? gt1 : gt0, odd ? ld1 : ld0, s);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
   }
 
   if (kj < n) {
