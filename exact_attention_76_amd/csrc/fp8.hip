@@ -461,6 +461,12 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? (LOOP == kLoopTwoStage ? 
   float m = -INFINITY;
   float l = 0.f;
   const float c = alpha * kLog2e;
+  // derived from m, updated only when m changes: the rescale threshold in units of the scores
+  // (m + kRescaleSlack / c; -inf while m is) and the exp2 offset m c - kPExp (m = -inf counts as
+  // 0, so fully masked rows give exp2(-inf) = 0 rather than NaN)
+  float thr = -INFINITY;
+  float mc = -(float)kPExp;
+  const float slack_s = kRescaleSlack / c;
   const int kv_end = CAUSAL ? min(n, q0 + BR) : n;  // keys any query of the workgroup sees
   static_assert(!WINDOW || CAUSAL, "a sliding window is causal");
   // the loop counts tiles from t0, the first one any query of the workgroup sees
@@ -512,17 +518,18 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? (LOOP == kLoopTwoStage ? 
     mt = halves_max(mt);
     // P' = 2^kPExp * exp2((s - m) c) must stay at or below 448 (largest e4m3): rescale once some
     // row's maximum exceeds the stabiliser by more than kRescaleSlack in the exp2 domain
-    // (2^(6 + 2.75) = 430.5).  A smaller kPExp leaves more slack, so rescales are rarer.
-    const float thr = (m == -INFINITY) ? -INFINITY : m * c + kRescaleSlack;
-    if (__builtin_amdgcn_ballot_w64(mt * c > thr)) {
+    // (2^(6 + 2.75) = 430.5; the 0.057 left to 448 = 2^8.807 covers the rounding of thr).  A
+    // smaller kPExp leaves more slack, so rescales are rarer.
+    if (__builtin_amdgcn_ballot_w64(mt > thr)) {
       const float mnew = fmaxf(m, mt);
       const float corr = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - mnew) * c);
       m = mnew;
       l *= corr;
 #pragma unroll
       for (int db = 0; db < 4; ++db) oacc[db] *= corr;
+      thr = m + slack_s;
+      mc = ((m == -INFINITY) ? 0.f : m * c) - (float)kPExp;
     }
-    const float mc = ((m == -INFINITY) ? 0.f : m * c) - (float)kPExp;
     float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int cb = 0; cb < NB_C; ++cb)
