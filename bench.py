@@ -61,9 +61,9 @@ MEASURED_TRAFFIC = {
     "bf16_mha16k": {"sources": {"exact_attention_76_amd/csrc/attn_fwd.hip": "549c7fde5c869bf2",
                                 _DEC: "5177b80538cd69cc", _T16: "91339639cbec1225"},
                     "bytes": 404107641},
-    "fp8_attention": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "af323a609afcc034",
+    "fp8_attention": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "804140349d467fa5",
                                   _DEC: "5177b80538cd69cc"}, "bytes": 186654602},
-    "fp8_prepare": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "af323a609afcc034"},
+    "fp8_prepare": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "804140349d467fa5"},
                     "bytes": 302650266},
 }
 

@@ -23,14 +23,14 @@
 //   * Attention (dense or packed sequences, causal or not, grouped-query heads): the plain loop
 //     of the 16-bit kernel (scores formed transposed, online softmax in fp32, K/V tiles copied
 //     buffer-to-LDS, two LDS stages, one barrier per tile) with four waves (128 queries) per
-//     workgroup and three workgroups per CU -- the softmax is the larger
-//     share here, and three free-running waves per SIMD hide its latencies better than the
-//     two-stage loop or the ping-pong of two waves (both built as loop shapes, both measured
-//     slower) -- and both products on v_mfma_scale_f32_32x32x64_f8f6f4.  A tile's K/V scales
-//     are loaded with its copy, one tile ahead, so no wait on a scale waits for a copy.  The per-block power-of-two scales of
-//     Q, K and V go into the instruction's E8M0 scale operands, so they cost nothing.  P is
-//     quantised as e4m3 of 2^6 * P (the 2^6 rides in the exp2 argument and cancels against the
-//     row sum, which is summed from the unquantised values).  V is read transposed from LDS
+//     workgroup and three workgroups per CU -- the softmax is the larger share here, and three
+//     free-running waves per SIMD hide its latencies better than the two-stage loop or the
+//     ping-pong of two waves (both built as loop shapes, both measured slower) -- and both
+//     products on v_mfma_scale_f32_32x32x64_f8f6f4.  A tile's K/V scales are loaded with its
+//     copy, one tile ahead, so no wait on a scale waits for a copy.  The per-block power-of-two
+//     scales of Q, K and V go into the instruction's E8M0 scale operands, so they cost nothing.
+//     P is quantised as e4m3 of 2^6 * P (the 2^6 rides in the exp2 argument and cancels against
+//     the row sum, which is summed from the unquantised values).  V is read transposed from LDS
 //     with ds_read_b64_tr_b8, the key order matching the byte order of the P operand.
 #include <hip/hip_runtime.h>
 #include <limits.h>
@@ -616,7 +616,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? (LOOP == kLoopTwoStage ? 
     // step), forms S_{j+1} from the K half of tile j+1, then takes the softmax of S_j and the
     // second product with the V half of tile j.  Its wait and barrier make tile j+2 visible
     // for step j+1.  The score registers alternate between sa and sb, so the loop is unrolled
-    // six times to name every buffer and register set statically.
+    // by six to name every buffer and register set statically.
     TileScales sc0, sc1, sc2;
     issue_tile(st0, t0, sc0);
     sc2 = sc1 = sc0;
