@@ -167,6 +167,11 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
   float m = -INFINITY;  // running max of raw scores q.k (the stabiliser; may trail the true max)
   float l = 0.f;        // running sum over this lane's keys (lane halves are added at the end)
   const float c = alpha * kLog2e;
+  // derived from m, updated only when m changes: the rescale threshold in units of the scores
+  // (m + 8 / c; -inf while m is) and the stabiliser m c (0 while m = -inf)
+  float thr = -INFINITY;
+  float mc_cur = 0.f;
+  const float slack_s = 8.f / c;
 
   static_assert(!WINDOW || CAUSAL, "a sliding window is causal");
   const int kv_end = CAUSAL ? min(n, q0 + BR) : n;
@@ -217,17 +222,18 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[cb][r]);
     mt = halves_max(mt);
     // Rescale only when some row's maximum grew by more than 2^8 in the exp2 domain; otherwise
-    // keep the old stabiliser (P then stays below 2^8).  O / l and L are exact either way.
-    const float thr = (m == -INFINITY) ? -INFINITY : m * c + 8.f;
-    if (__builtin_amdgcn_ballot_w64(mt * c > thr)) {
+    // keep the old stabiliser (P then stays below about 2^8).  O / l and L are exact either way.
+    if (__builtin_amdgcn_ballot_w64(mt > thr)) {
       const float mnew = fmaxf(m, mt);
       const float corr = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - mnew) * c);
       m = mnew;
       l *= corr;
 #pragma unroll
       for (int db = 0; db < NB_D; ++db) oacc[db] *= corr;
+      thr = m + slack_s;
+      mc_cur = (m == -INFINITY) ? 0.f : m * c;
     }
-    return (m == -INFINITY) ? 0.f : m * c;
+    return mc_cur;
   };
   // O^T += V^T P^T for one k-step (16 keys): accumulator registers 8*(st%2) .. +7 of block st/2
   auto gemm2_step = [&](const char* vs, int st, u32x4 pf) {
