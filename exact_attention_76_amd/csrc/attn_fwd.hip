@@ -220,10 +220,12 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
     for (int cb = 0; cb < NB_C; ++cb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[cb][r]);
-    mt = halves_max(mt);
     // Rescale only when some row's maximum grew by more than 2^8 in the exp2 domain; otherwise
     // keep the old stabiliser (P then stays below about 2^8).  O / l and L are exact either way.
+    // The test needs no row maximum: some lane's maximum over its half of the keys exceeds the
+    // threshold exactly when some row's does.  The branch is uniform, so the lane swap is safe.
     if (__builtin_amdgcn_ballot_w64(mt > thr)) {
+      mt = halves_max(mt);
       const float mnew = fmaxf(m, mt);
       const float corr = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - mnew) * c);
       m = mnew;
@@ -251,7 +253,7 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
     f32x16 s[NB_C];
     gemm1(ks, s);
     const float mc = update_max(s, j);
-    float rs0 = 0.f, rs1 = 0.f;
+    float rs0 = -0.f, rs1 = -0.f;  // -0 + p = p exactly, so the first adds fold away
     if constexpr (SH::EXPFIRST) {
 #pragma unroll
       for (int cb = 0; cb < NB_C; ++cb)
@@ -395,7 +397,7 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
       else copy(vbase, vdst, j + 1);
       if (j >= jlo && j < jw) {
         const float mc = update_max(s, j);
-        float rs0 = 0.f, rs1 = 0.f;
+        float rs0 = -0.f, rs1 = -0.f;  // -0 + p = p exactly, so the first adds fold away
 #pragma unroll
         for (int st = 0; st < KS_C; ++st) {
           const int cb = st >> 1, base = (st & 1) * 8;

@@ -515,12 +515,14 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? (LOOP == kLoopTwoStage ? 
     for (int cb = 0; cb < NB_C; ++cb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[cb][r]);
-    mt = halves_max(mt);
     // P' = 2^kPExp * exp2((s - m) c) must stay at or below 448 (largest e4m3): rescale once some
     // row's maximum exceeds the stabiliser by more than kRescaleSlack in the exp2 domain
     // (2^(6 + 2.75) = 430.5; the 0.057 left to 448 = 2^8.807 covers the rounding of thr).  A
-    // smaller kPExp leaves more slack, so rescales are rarer.
+    // smaller kPExp leaves more slack, so rescales are rarer.  The test needs no row maximum:
+    // some lane's maximum over its half of the keys exceeds the threshold exactly when some
+    // row's does.  The branch is uniform, so the lane swap is safe.
     if (__builtin_amdgcn_ballot_w64(mt > thr)) {
+      mt = halves_max(mt);
       const float mnew = fmaxf(m, mt);
       const float corr = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - mnew) * c);
       m = mnew;
@@ -530,7 +532,7 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? (LOOP == kLoopTwoStage ? 
       thr = m + slack_s;
       mc = ((m == -INFINITY) ? 0.f : m * c) - (float)kPExp;
     }
-    float rs0 = 0.f, rs1 = 0.f;
+    float rs0 = -0.f, rs1 = -0.f;  // -0 + p = p exactly, so the first adds fold away
 #pragma unroll
     for (int cb = 0; cb < NB_C; ++cb)
 #pragma unroll
