@@ -58,13 +58,13 @@ HBM_PEAK_GBS = 8000.0
 _DEC = "exact_attention_76_amd/csrc/decompose.h"
 _T16 = "exact_attention_76_amd/csrc/tile16.h"
 MEASURED_TRAFFIC = {
-    "bf16_mha16k": {"sources": {"exact_attention_76_amd/csrc/attn_fwd.hip": "89a1efde5c9bad70",
+    "bf16_mha16k": {"sources": {"exact_attention_76_amd/csrc/attn_fwd.hip": "bd528510bdf5b216",
                                 _DEC: "5177b80538cd69cc", _T16: "91339639cbec1225"},
-                    "bytes": 404089647},
-    "fp8_attention": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "804140349d467fa5",
-                                  _DEC: "5177b80538cd69cc"}, "bytes": 186654602},
-    "fp8_prepare": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "804140349d467fa5"},
-                    "bytes": 302650266},
+                    "bytes": 404033298},
+    "fp8_attention": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "c0a0703a5213dee5",
+                                  _DEC: "5177b80538cd69cc"}, "bytes": 185831635},
+    "fp8_prepare": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "c0a0703a5213dee5"},
+                    "bytes": 302659534},
 }
 
 
