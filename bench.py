@@ -61,10 +61,10 @@ MEASURED_TRAFFIC = {
     "bf16_mha16k": {"sources": {"exact_attention_76_amd/csrc/attn_fwd.hip": "bd528510bdf5b216",
                                 _DEC: "5177b80538cd69cc", _T16: "91339639cbec1225"},
                     "bytes": 404033298},
-    "fp8_attention": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "c0a0703a5213dee5",
-                                  _DEC: "5177b80538cd69cc"}, "bytes": 185831635},
-    "fp8_prepare": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "c0a0703a5213dee5"},
-                    "bytes": 302659534},
+    "fp8_attention": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "88d8095301d0ddf6",
+                                  _DEC: "5177b80538cd69cc"}, "bytes": 185894200},
+    "fp8_prepare": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "88d8095301d0ddf6"},
+                    "bytes": 302676234},
 }
 
 

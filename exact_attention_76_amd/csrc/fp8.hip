@@ -477,21 +477,21 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? (LOOP == kLoopTwoStage ? 
     return !CAUSAL || (k0 <= qw + 31 && (!WINDOW || k0 + BC - 1 > qw - window));
   };
 
-  // first product of loop tile j: S^T = K Q^T from the K half of its buffer
+  // first product of loop tile j: S^T = K Q^T from the K half of its buffer; the two 32-key
+  // blocks alternate, so consecutive matrix instructions do not depend on each other
   auto gemm1 = [&](const char* stage, const TileScales& sc, f32x16* s) {
     const char* kt = stage;
 #pragma unroll
-    for (int cb = 0; cb < NB_C; ++cb) {
-      const int sk = e8m0_of(sc.k[cb >> 1]);
-      s[cb] = f32x16{};
+    for (int st = 0; st < 2; ++st)
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+      for (int cb = 0; cb < NB_C; ++cb) {
+        const int sk = e8m0_of(sc.k[cb >> 1]);
+        if (st == 0) s[cb] = f32x16{};
         const u32x4 a0 = *reinterpret_cast<const u32x4*>(kt + koff[0] + cb * 4096 + st * 1024);
         const u32x4 a1 = *reinterpret_cast<const u32x4*>(kt + koff[1] + cb * 4096 + st * 1024);
         const i32x8 a = i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
         s[cb] = mma_f8(a, qf[st], s[cb], sk, sq);
       }
-    }
   };
   // mask and online softmax of loop tile j (scores s), packed into the e4m3 B operands pf of the
   // second product
