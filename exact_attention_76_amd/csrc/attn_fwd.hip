@@ -336,7 +336,9 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
     f32x16 s[NB_C];
     u32x4 pf[KS_C];
     // An M phase is one stream of products (the second product of the previous tile, then the
-    // first product of this tile) whose LDS operands are read PD products ahead.
+    // first product of this tile) whose LDS operands are read PD products ahead.  In the first
+    // product the 32-key blocks alternate, so consecutive matrix instructions do not accumulate
+    // into the same registers.
     constexpr int N2 = KS_C * NB_D, N1 = NB_C * KS_D, PD = SH::PD;
     auto operand = [&](const char* ks, const char* vs, int i) -> u32x4 {
       if (i < N2) {
@@ -347,7 +349,7 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
         const u32x2 a0 = __builtin_bit_cast(u32x2, t0), a1 = __builtin_bit_cast(u32x2, t1);
         return u32x4{a0[0], a0[1], a1[0], a1[1]};
       }
-      const int cb = (i - N2) / KS_D, st = (i - N2) % KS_D;
+      const int cb = (i - N2) % NB_C, st = (i - N2) / NB_C;
       return *reinterpret_cast<const u32x4*>(ks + koff[st & 1] + cb * 512 * NCH + 512 * (st & ~1));
     };
     auto product = [&](int i, u32x4 a) {
@@ -355,7 +357,7 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
         const int st = i / NB_D, db = i % NB_D;
         oacc[db] = mma32<BF16>(a, pf[st], oacc[db]);
       } else {
-        const int cb = (i - N2) / KS_D, st = (i - N2) % KS_D;
+        const int cb = (i - N2) % NB_C, st = (i - N2) / NB_C;
         if (st == 0) s[cb] = f32x16{};
         s[cb] = mma32<BF16>(a, qf[st], s[cb]);
       }
