@@ -61,10 +61,10 @@ MEASURED_TRAFFIC = {
     "bf16_mha16k": {"sources": {"exact_attention_76_amd/csrc/attn_fwd.hip": "ee3128d159a6e036",
                                 _DEC: "5177b80538cd69cc", _T16: "91339639cbec1225"},
                     "bytes": 403999164},
-    "fp8_attention": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "88d8095301d0ddf6",
-                                  _DEC: "5177b80538cd69cc"}, "bytes": 185894200},
-    "fp8_prepare": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "88d8095301d0ddf6"},
-                    "bytes": 302676234},
+    "fp8_attention": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "11506b4cbf68a36c",
+                                  _DEC: "5177b80538cd69cc"}, "bytes": 185916504},
+    "fp8_prepare": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "11506b4cbf68a36c"},
+                    "bytes": 302622270},
 }
 
 

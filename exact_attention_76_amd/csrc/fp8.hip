@@ -89,6 +89,18 @@ __device__ __forceinline__ double shfl_xor_d(double x, int mask) {
   return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
 
+// The value of lane (lane ^ M) of the same quad, M = 1 or 2: two DPP quad permutations (a
+// vector-ALU move with no LDS round trip).  Every lane of the wave must be active.
+template <int M>
+__device__ __forceinline__ double quad_xor_d(double x) {
+  static_assert(M == 1 || M == 2, "quad partner");
+  constexpr int kQuadPerm = M == 1 ? 0xB1 : 0x4E;  // source lanes [1,0,3,2] / [2,3,0,1]
+  const long long v = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(v & 0xffffffff), kQuadPerm, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(v >> 32), kQuadPerm, 0xF, 0xF, true);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
 // Smallest exponent of a normal fp32 scale.
 constexpr int kScaleExpMin = -126;
 
@@ -195,15 +207,16 @@ __global__ __launch_bounds__(256) void fp8_prepare_kernel(PrepTensor t0, PrepTen
           y[i] = a + c;
           y[i + hs] = a - c;
         }
+    // strides 32 and 64: partner lane p ^ 1, then p ^ 2, in the same quad.  The lower lane
+    // keeps a + b and the upper lane a - b, each as fma(+-1, own, partner): one rounding, the
+    // same as the add or subtract.
+    auto cross = [&](auto xchg, int m) {
+      const double sg = (p & m) ? -1.0 : 1.0;
 #pragma unroll
-    for (int m = 1; m <= 2; m <<= 1) {  // strides 32 and 64: partner lane p ^ m
-      const bool upper = (p & m) != 0;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const double o = shfl_xor_d(y[i], m);
-        y[i] = upper ? o - y[i] : y[i] + o;
-      }
-    }
+      for (int i = 0; i < 32; ++i) y[i] = __builtin_fma(sg, y[i], xchg(y[i]));
+    };
+    cross([](double x) { return quad_xor_d<1>(x); }, 1);
+    cross([](double x) { return quad_xor_d<2>(x); }, 2);
   }
   int e;
   if constexpr (PASS == kPrepTensorCodes) {
