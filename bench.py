@@ -18,10 +18,6 @@ sweep's aggregate (total FLOPs over total time).  ``--workload`` selects the oth
           non-causal) and the causal d=128 inputs (B=2 N=8192); FLOPs = 2.5 x the forward's
   window  causal sliding window of 4096 keys, B=1 N=16384 H=16 d=128 (the headline's inputs), bf16
           then e4m3; FLOPs count the visible pairs, n^2/2 - (n-W)^2/2 per head
-  ceiling the matrix-core ceiling the attention kernels run against: back-to-back
-          v_mfma_f32_32x32x16_bf16 on random operands on every CU (2 and 4 waves per SIMD),
-          with no LDS or vector-ALU work; under the chip's power limit this sits well below
-          the nominal dense peak
 
 Metric (FlashAttention-3 digest, section 7.1): TFLOPs/s with FLOPs = 4 * B * H * N^2 * d
 (halved when causal; summed per sequence for packed inputs), and the fraction of MI355X dense
@@ -88,7 +84,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mha16k", choices=["mha16k", "sweep", "causal", "varlen", "fp8", "fp8_causal",
-                                                              "fp8_varlen", "window", "bwd", "ceiling"])
+                                                              "fp8_varlen", "window", "bwd"])
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
@@ -332,52 +328,6 @@ def run_bwd(args, name, inp, dev, stream):
                 extra={"pass": "backward", "flops_rule": "2.5 x forward (five products)"})
 
 
-def run_ceiling(args, dev, stream):
-    import ctypes
-
-    import torch
-
-    lib = ctypes.CDLL(os.path.join(ROOT, "exact_attention_76_amd", "libceiling.so"))
-    for fn in (lib.ceiling_mfma_bf16, lib.ceiling_mfma_fp8):
-        fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(7)
-    normal = torch.randn(65536 * 8, device=dev, generator=gen)  # 1 MiB of bf16, or 512 KiB x 2 of e4m3
-    srcs = {"bf16": normal.to(torch.bfloat16),
-            "fp8": normal.to(torch.float8_e4m3fn).view(torch.uint8).repeat(2)}  # finite codes only
-    kinds = {"bf16": (lib.ceiling_mfma_bf16, 32 * 32 * 16 * 2, "v_mfma_f32_32x32x16_bf16"),
-             "fp8": (lib.ceiling_mfma_fp8, 32 * 32 * 64 * 2, "v_mfma_scale_f32_32x32x64_f8f6f4")}
-    out = []
-    for dtype, (fn, flop_per_instr, instr) in kinds.items():
-        iters = 4000 if dtype == "bf16" else 2000
-        for waves_per_simd, grid in ((2, 512), (4, 1024)):
-            sink = torch.empty(grid * 256, dtype=torch.float32, device=dev)
-            src = srcs[dtype]
-
-            def step():
-                rc = fn(src.data_ptr(), sink.data_ptr(), iters, grid, stream.cuda_stream)
-                if rc != 0:
-                    raise RuntimeError(f"{instr} ceiling probe failed with hipError {rc}")
-
-            steps, warmup = max(1, min(args.steps, 10)), max(1, min(args.warmup, 5))
-            ms_wall, ms_gpu = timed(step, stream, steps, warmup)
-            flops = grid * 4 * iters * 8 * flop_per_instr
-            achieved = flops / (ms_gpu * 1e-3) / 1e12
-            out.append({
-                "metric": f"sustained {instr} throughput on random operands (matrix-core ceiling)",
-                "value": round(flops / (ms_wall * 1e-3) / 1e12, 2), "unit": "TFLOP/s", "n_gpus": 1,
-                "steps": steps, "warmup": warmup, "ms_per_step": round(ms_wall, 4), "higher_is_better": True,
-                "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
-                "config": {"workload": f"mfma_{dtype}_ceiling_{waves_per_simd}_waves_per_simd", "workgroups": grid,
-                           "waves_per_simd": waves_per_simd, "instructions_per_wave": 8 * iters,
-                           "pct_of_peak": round(100 * achieved / PEAK[dtype], 2), "parallelism": "single GPU"},
-                "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK[dtype], "unit": "TFLOP/s",
-                             "frac": round(achieved / PEAK[dtype], 4), "traffic": None},
-                "cpu_baseline": None,
-            })
-    return out
-
-
 def main():
     args = parse()
     if args.gpus != 1:
@@ -429,11 +379,9 @@ def main():
         elif args.workload == "bwd":
             out = [run_bwd(args, "bwd_" + n, si.CONFIGS[n](), dev, stream)
                    for n in ("mha_n16384_b1_h16_d128", "causal_b2_h16_n8192_d128")]
-        elif args.workload == "window":
+        else:  # window
             out = [run_16bit(args, f"window{WINDOW}_b1_h16_n16384_d128", window_inputs(), dev, stream),
                    run_fp8(args, dev, stream, "mha_n16384_b1_h16_d128", inp=window_inputs())]
-        else:
-            out = run_ceiling(args, dev, stream)
     for o in out:
         print(json.dumps(o), flush=True)
 

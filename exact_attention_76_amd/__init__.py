@@ -21,6 +21,7 @@ Helpers :func:`attention` and :func:`fp8_prepare` allocate the outputs and call 
 from __future__ import annotations
 
 import ctypes
+import json
 import os
 import re
 
@@ -47,8 +48,28 @@ class AttnError(RuntimeError):
         self.status = status
 
 
+def check_build_record() -> None:
+    """Raise unless libattn.so was built from the sources now on disk: build() records the sha256
+    of every source file (and the extra compiler arguments) beside the library."""
+    from . import build as _build
+
+    try:
+        with open(_build.RECORD) as f:
+            built = json.load(f)
+    except (OSError, ValueError) as e:
+        raise OSError(f"{LIB_PATH} has no readable source record ({_build.RECORD}): rebuild it "
+                      "with exact_attention_76_amd/build.py") from e
+    now = _build.source_record()
+    stale = sorted(set(built.get("sources", {}).items()) ^ set(now["sources"].items()))
+    if stale or built.get("extra_flags", "") != now["extra_flags"]:
+        what = sorted({name for name, _ in stale}) or [f"compiler arguments {built.get('extra_flags')!r}"]
+        raise OSError(f"{LIB_PATH} was not built from the sources on disk (differs in {what}): rebuild it "
+                      "with exact_attention_76_amd/build.py")
+
+
 def load_library(build_if_missing: bool = True):
-    """Load libattn.so; compile it first only when no built library exists."""
+    """Load libattn.so; compile it first only when no built library exists.  A library built
+    from other sources than those on disk is refused (see check_build_record)."""
     global _lib
     if _lib is not None:
         return _lib
@@ -58,6 +79,7 @@ def load_library(build_if_missing: bool = True):
         from . import build as _build
 
         _build.build()
+    check_build_record()
     lib = ctypes.CDLL(LIB_PATH)
     P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.attn_fwd.argtypes = [P, P, P, P, P, I, I, I, I, P, I, I, F, I, P, P, P, P]

@@ -1,8 +1,14 @@
-"""Build libattn.so (the attention path: api, attn_fwd, fp8) and libceiling.so (the matrix-core
-throughput probe that bench.py reports beside the attention figures) for gfx950 with hipcc."""
+"""Build libattn.so (the attention path: api, attn_fwd, attn_bwd, fp8) for gfx950 with hipcc.
+
+Beside the library, build() writes libattn.so.sources.json: the sha256 of every source file the
+library was compiled from (csrc/*, include/attn.h) and the extra compiler arguments.
+load_library() refuses a library whose record does not match the sources on disk, so the tests,
+the smoke check and the benchmark always run the code that is in the tree."""
 from __future__ import annotations
 
 import concurrent.futures
+import hashlib
+import json
 import os
 import subprocess
 import sys
@@ -13,16 +19,16 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJ_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
+RECORD = LIB + ".sources.json"
 SOURCES = ["api.hip", "attn_fwd.hip", "attn_bwd.hip", "fp8.hip"]
-CEILING_LIB = os.path.join(PKG, "libceiling.so")
-CEILING_SOURCES = ["ceiling.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: hipcc must not form v_pk_{add,mul,fma}_f32 from scalar or float2 code.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
 # Extra compiler arguments (whitespace-separated), e.g. a different loop shape for an ablation run:
-#   ATTN_HIPCC_EXTRA='-DATTN_D128_SHAPE=64,attn::LoopShape<8,true>' python exact_attention_76_amd/build.py
+#   ATTN_HIPCC_EXTRA='-DATTN_D128_SHAPE=64,attn::LoopShape<8>' python exact_attention_76_amd/build.py
+# (load_library() then loads that library only while ATTN_HIPCC_EXTRA holds the same arguments)
 FLAGS += os.environ.get("ATTN_HIPCC_EXTRA", "").split()
 
 
@@ -44,15 +50,26 @@ def _link(objs: list[str], lib: str) -> None:
     os.replace(tmp, lib)
 
 
+def source_record() -> dict:
+    """sha256 of every file the library is compiled from, and the extra compiler arguments."""
+    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".h")))
+    rec = {f"csrc/{f}": hashlib.sha256(open(os.path.join(CSRC, f), "rb").read()).hexdigest() for f in files}
+    rec["include/attn.h"] = hashlib.sha256(open(os.path.join(INCLUDE, "attn.h"), "rb").read()).hexdigest()
+    return {"sources": rec, "extra_flags": os.environ.get("ATTN_HIPCC_EXTRA", "")}
+
+
 def build() -> str:
-    """Compile every source (in parallel) and link libattn.so and libceiling.so in the package
-    directory; returns the path of libattn.so."""
+    """Compile every source (in parallel), link libattn.so in the package directory and write
+    its source record; returns the path of libattn.so."""
     os.makedirs(OBJ_DIR, exist_ok=True)
-    sources = SOURCES + CEILING_SOURCES
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(sources)) as ex:
-        objs = dict(zip(sources, ex.map(_compile, sources)))
-    _link([objs[s] for s in SOURCES], LIB)
-    _link([objs[s] for s in CEILING_SOURCES], CEILING_LIB)
+    record = source_record()
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    _link(objs, LIB)
+    tmp = RECORD + ".tmp"
+    with open(tmp, "w") as f:
+        json.dump(record, f, indent=1, sort_keys=True)
+    os.replace(tmp, RECORD)
     return LIB
 
 

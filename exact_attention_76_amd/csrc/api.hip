@@ -24,6 +24,11 @@ int validate_common(const void* q, const void* k, const void* v, const void* o, 
   return ATTN_OK;
 }
 
+// Clears an error that earlier, unrelated HIP work left pending, so that the launches of this
+// call are judged by their own hipGetLastError().  Called once, after validation and before the
+// first launch.
+void clear_pending_error() { (void)hipGetLastError(); }
+
 int status_of(hipError_t err) {
   if (err == hipSuccess) return ATTN_OK;
   if (err == hipErrorNotSupported) return ATTN_ERR_UNSUPPORTED;
@@ -48,12 +53,14 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
       if (d != 64 && d != 128 && d != 256) return ATTN_ERR_UNSUPPORTED;
       // the kernels address one head's K/V rows with 32-bit byte offsets
       if ((long long)N * Hkv * d * 2 > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
+      clear_pending_error();
       err = attn::launch_fwd_16bit(a, dtype == ATTN_BF16, stream);
       break;
     case ATTN_FP8_E4M3:
       if (!q_scale || !k_scale || !v_scale) return ATTN_ERR_INVALID;
       if (d != 128) return ATTN_ERR_UNSUPPORTED;
       if ((long long)N * Hkv * d > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;
+      clear_pending_error();
       err = attn::launch_fwd_fp8(a, stream);
       break;
     default:
@@ -79,6 +86,7 @@ int bwd(const void* q, const void* k, const void* v, const void* o, const float*
       !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
     return ATTN_ERR_ALIGN;
   attn::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, cu_seqlens, d, causal, window, alpha};
+  clear_pending_error();
   return status_of(attn::launch_bwd_16bit(a, dtype == ATTN_BF16, stream));
 }
 
@@ -157,6 +165,7 @@ int attn_fp8_prepare_ex(const void* q, const void* k, const void* v, void* q8, v
     return ATTN_ERR_ALIGN;
   attn::PrepareArgs a{q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, B, Hq, Hkv, N, d, cu_seqlens, hadamard_signs,
                       scaling == ATTN_FP8_SCALE_TENSOR, rope_cos, rope_sin};
+  clear_pending_error();
   return status_of(attn::launch_fp8_prepare(a, stream));
 }
 

@@ -9,8 +9,8 @@
 //
 // gfx950 mapping (ours):
 //   * bwd_delta_kernel: D per (query, head), one 16-byte slice of dO and O per lane.
-//   * bwd_dkdv_kernel: a workgroup of four waves owns 128 keys of one (sequence, key/value head),
-//     32 per wave; its K and V rows stay in registers as matrix-instruction B operands (one key
+//   * bwd_dkdv_kernel: a workgroup of kKvWaves waves (eight: two per SIMD) owns 32 keys per
+//     wave (256) of one (sequence, key/value head); its K and V rows stay in registers as matrix-instruction B operands (one key
 //     per lane column).  It walks the query tiles of every query head of the group: Q and dO
 //     tiles (and their L and D values) are copied buffer-to-LDS, two stages deep, and each
 //     tile takes S = Q K^T and dP = dO V^T (A operands read from the tile rows), P and dS in

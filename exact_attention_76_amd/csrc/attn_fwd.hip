@@ -43,16 +43,15 @@ namespace {
 
 // Tile-loop shape of one (d, BC) instance:
 //   WAVES     waves per workgroup, 32 queries each (the workgroup owns 32 * WAVES queries);
-//   EXPFIRST  take all exponentials of a tile before its second product, instead of one
-//             k-step at a time next to that k-step's products.
 //   PP        ping-pong: the waves of the two halves of the workgroup (one of each per SIMD)
 //             run one phase apart, so that one half's products and the other half's softmax
-//             occupy a SIMD at the same time (see the main loop).
+//             occupy a SIMD at the same time (see the main loop).  Otherwise the plain loop,
+//             which takes a tile's exponentials one k-step at a time next to that k-step's
+//             products.
 //   PD        (ping-pong only) how many products ahead the LDS operand reads are issued.
-template <int WAVES_, bool EXPFIRST_, bool PP_ = false, int PD_ = 4>
+template <int WAVES_, bool PP_ = false, int PD_ = 4>
 struct LoopShape {
   static constexpr int WAVES = WAVES_;
-  static constexpr bool EXPFIRST = EXPFIRST_;
   static constexpr bool PP = PP_;
   static constexpr int PD = PD_;
 };
@@ -254,28 +253,14 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
     gemm1(ks, s);
     const float mc = update_max(s, j);
     float rs0 = -0.f, rs1 = -0.f;  // -0 + p = p exactly, so the first adds fold away
-    if constexpr (SH::EXPFIRST) {
-#pragma unroll
-      for (int cb = 0; cb < NB_C; ++cb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cb][r], c, -mc));
-          s[cb][r] = p;
-          if (r & 1) rs1 += p; else rs0 += p;
-        }
-    }
 #pragma unroll
     for (int st = 0; st < KS_C; ++st) {
       const int cb = st >> 1, base = (st & 1) * 8;
       float p[8];
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        if constexpr (SH::EXPFIRST) {
-          p[t] = s[cb][base + t];
-        } else {
-          p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cb][base + t], c, -mc));
-          if (t & 1) rs1 += p[t]; else rs0 += p[t];
-        }
+        p[t] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[cb][base + t], c, -mc));
+        if (t & 1) rs1 += p[t]; else rs0 += p[t];
       }
       gemm2_step(vs, st, u32x4{pack2<BF16>(p[0], p[1]), pack2<BF16>(p[2], p[3]), pack2<BF16>(p[4], p[5]),
                                pack2<BF16>(p[6], p[7])});
@@ -508,16 +493,16 @@ hipError_t launch_window(const FwdArgs& a, hipStream_t stream) {
 // VALU freely, is as fast.  With a sliding window, d = 256 runs the plain loop: the window's
 // bookkeeping does not fit the ping-pong loop's 256 registers without spilling.
 #ifndef ATTN_D64_SHAPE
-#define ATTN_D64_SHAPE 64, LoopShape<8, false>
+#define ATTN_D64_SHAPE 64, LoopShape<8>
 #endif
 #ifndef ATTN_D128_SHAPE
-#define ATTN_D128_SHAPE 64, LoopShape<8, true, true, 3>
+#define ATTN_D128_SHAPE 64, LoopShape<8, true, 3>
 #endif
 #ifndef ATTN_D256_SHAPE
-#define ATTN_D256_SHAPE 32, LoopShape<8, false, true, 4>
+#define ATTN_D256_SHAPE 32, LoopShape<8, true, 4>
 #endif
 #ifndef ATTN_D256_WINDOW_SHAPE
-#define ATTN_D256_WINDOW_SHAPE 32, LoopShape<8, false>
+#define ATTN_D256_WINDOW_SHAPE 32, LoopShape<8>
 #endif
 
 template <bool BF16>

@@ -1,4 +1,4 @@
-// decompose.h -- work decomposition shared by the attention kernels (device code): which
+// decompose.h -- work decomposition shared by the attention kernels (host and device code): which
 // (sequence, head, query block) a workgroup computes.  The FlashAttention-3 pages parallelise the
 // forward pass over batch x head x query blocks, one block of O per thread block (zenmind
 // digest, section 4, data path step 1); the mapping below also places that work on gfx950's 8
@@ -11,7 +11,7 @@ namespace attn {
 
 // Bijection from hardware workgroup id to a logical id such that each XCD (hardware id mod 8)
 // receives one contiguous range of logical ids.
-__device__ __forceinline__ int xcd_remap(int wg, int total) {
+__host__ __device__ __forceinline__ int xcd_remap(int wg, int total) {
   constexpr int kXcd = 8;
   const int q = total / kXcd, r = total % kXcd;
   const int x = wg % kXcd, i = wg / kXcd;
@@ -27,7 +27,7 @@ __device__ __forceinline__ int xcd_remap(int wg, int total) {
 // its index); non-causal grids keep the blocks of one head together.  Otherwise each XCD
 // takes one contiguous range of (sequence, head, block) ids, causal blocks longest first.
 template <bool CAUSAL>
-__device__ __forceinline__ void decompose(int wg, int nqb, int Hq, int Hkv, int B, int& qb, int& h, int& b) {
+__host__ __device__ __forceinline__ void decompose(int wg, int nqb, int Hq, int Hkv, int B, int& qb, int& h, int& b) {
   constexpr int kXcd = 8;
   if (Hq % kXcd == 0) {
     const int x = wg % kXcd, slot = wg / kXcd;

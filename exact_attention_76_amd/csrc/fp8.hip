@@ -24,9 +24,9 @@
 //     of the 16-bit kernel (scores formed transposed, online softmax in fp32, K/V tiles copied
 //     buffer-to-LDS, two LDS stages, one barrier per tile) with four waves (128 queries) per
 //     workgroup and three workgroups per CU -- the softmax is the larger share here, and three
-//     free-running waves per SIMD hide its latencies better than the two-stage loop or the
-//     ping-pong of two waves (both built as loop shapes, both measured slower) -- and both
-//     products on v_mfma_scale_f32_32x32x64_f8f6f4.  A tile's K/V scales are loaded with its
+//     free-running waves per SIMD hide its latencies better than a two-stage loop or a ping-pong
+//     of two waves (both measured slower on MI355X) -- and both products on
+//     v_mfma_scale_f32_32x32x64_f8f6f4.  A tile's K/V scales are loaded with its
 //     copy, one tile ahead, so no wait on a scale waits for a copy.  The per-block power-of-two
 //     scales of Q, K and V go into the instruction's E8M0 scale operands, so they cost nothing.
 //     P is quantised as e4m3 of 2^6 * P (the 2^6 rides in the exp2 argument and cancels against
@@ -349,21 +349,10 @@ static_assert(kPExp + kRescaleSlack <= 8.807f, "2^(kPExp + kRescaleSlack) must n
 // 64-token scale block).  CAUSAL: key j visible to query i iff j <= i.  VARLEN: packed sequences
 // [T, H, d] delimited by cu_seqlens, scale blocks counted from each sequence's first token.
 // WINDOW (implies CAUSAL): query i sees keys i-window+1 .. i only.
-// LOOP selects the tile loop:
-//   kLoopOne      one stage per tile (two K/V buffers, three waves per SIMD with four waves per
-//                 workgroup; co-resident waves interleave freely);
-//   kLoopTwoStage each wave issues the first product of tile j+1 before the softmax of tile j,
-//                 so the matrix core works on the next tile while the vector ALUs take the
-//                 exponentials of this one (three K/V buffers, two waves per SIMD);
-//   kLoopPingPong eight waves: the two halves of the workgroup (one wave of each per SIMD) run
-//                 one phase apart, products against softmax (three K and three V buffers).
-constexpr int kLoopOne = 0, kLoopTwoStage = 1, kLoopPingPong = 2;
-
-// Workgroup barrier between ping-pong phases.  The asm statement is a compiler memory barrier
-// (no LDS access moves across it); this wave's LDS reads are complete before it arrives.
-__device__ __forceinline__ void phase_barrier8() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-template <int WAVES, int BC, int LOOP, bool CAUSAL, bool VARLEN, bool WINDOW>
-__global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? (LOOP == kLoopTwoStage ? 2 : 3) : 1)) void fwd_fp8_kernel(
+// One stage per tile: two K/V buffers, one barrier per tile; with four waves per workgroup three
+// workgroups share a CU (three waves per SIMD), and co-resident waves interleave freely.
+template <int WAVES, int BC, bool CAUSAL, bool VARLEN, bool WINDOW>
+__global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? 3 : 1)) void fwd_fp8_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
     const float* __restrict__ qs, const float* __restrict__ ks_, const float* __restrict__ vs_,
     uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int N, const int* __restrict__ cu_seqlens,
@@ -374,18 +363,8 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? (LOOP == kLoopTwoStage ? 
   constexpr int NB_C = BC / 32;         // 32-key score blocks per tile
   constexpr int KS = BC / 64;           // 64-key k-steps of the second product
   static_assert(BC % 64 == 0 && NI >= 1 && NI * WAVES * 1024 == TILE, "tile shape");
-  static_assert(LOOP != kLoopPingPong || (WAVES == 8 && BC == 64), "ping-pong: eight waves, 64-key tiles");
-  constexpr bool PP = LOOP == kLoopPingPong;
-  __shared__ __attribute__((aligned(1024))) char st0[PP ? 1 : 2 * TILE];
-  __shared__ __attribute__((aligned(1024))) char st1[PP ? 1 : 2 * TILE];
-  __shared__ __attribute__((aligned(1024))) char st2[LOOP == kLoopTwoStage ? 2 * TILE : 1];
-  // ping-pong: K and V tiles in separate objects, so the compiler can tell them apart
-  __shared__ __attribute__((aligned(1024))) char kb0[PP ? TILE : 1];
-  __shared__ __attribute__((aligned(1024))) char kb1[PP ? TILE : 1];
-  __shared__ __attribute__((aligned(1024))) char kb2[PP ? TILE : 1];
-  __shared__ __attribute__((aligned(1024))) char vb0[PP ? TILE : 1];
-  __shared__ __attribute__((aligned(1024))) char vb1[PP ? TILE : 1];
-  __shared__ __attribute__((aligned(1024))) char vb2[PP ? TILE : 1];
+  __shared__ __attribute__((aligned(1024))) char st0[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) char st1[2 * TILE];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -601,204 +580,28 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? (LOOP == kLoopTwoStage ? 
   // causal: a wave skips the tiles that lie wholly above its diagonal or before its window; it
   // still copies and waits.  A lane whose keys in a tile are all masked keeps m = -inf and adds
   // nothing (P = exp2(-inf) = 0).
-  if constexpr (LOOP == kLoopOne) {
-    TileScales sc0, sc1;  // scales of the tiles in st0 and st1
-    issue_tile(st0, t0, sc0);
-    sc1 = sc0;
+  TileScales sc0, sc1;  // scales of the tiles in st0 and st1
+  issue_tile(st0, t0, sc0);
+  sc1 = sc0;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  f32x16 s[NB_C];
+  for (int j = 0; j < ntiles; j += 2) {
+    if (j + 1 < ntiles) issue_tile(st1, t0 + j + 1, sc1);
+    if (wave_needs(j)) {
+      gemm1(st0, sc0, s);
+      softmax_gemm2(st0, j, sc0, s);
+    }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    f32x16 s[NB_C];
-    for (int j = 0; j < ntiles; j += 2) {
-      if (j + 1 < ntiles) issue_tile(st1, t0 + j + 1, sc1);
-      if (wave_needs(j)) {
-        gemm1(st0, sc0, s);
-        softmax_gemm2(st0, j, sc0, s);
-      }
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (j + 1 >= ntiles) break;
-      if (j + 2 < ntiles) issue_tile(st0, t0 + j + 2, sc0);
-      if (wave_needs(j + 1)) {
-        gemm1(st1, sc1, s);
-        softmax_gemm2(st1, j + 1, sc1, s);
-      }
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
+    if (j + 1 >= ntiles) break;
+    if (j + 2 < ntiles) issue_tile(st0, t0 + j + 2, sc0);
+    if (wave_needs(j + 1)) {
+      gemm1(st1, sc1, s);
+      softmax_gemm2(st1, j + 1, sc1, s);
     }
-  } else if constexpr (LOOP == kLoopTwoStage) {
-    // Loop tile j lives in buffer j % 3.  Step j copies tile j+2 into the buffer of tile j-1
-    // (whose last reads, the second product of step j-1, ended before the barrier closing that
-    // step), forms S_{j+1} from the K half of tile j+1, then takes the softmax of S_j and the
-    // second product with the V half of tile j.  Its wait and barrier make tile j+2 visible
-    // for step j+1.  The score registers alternate between sa and sb, so the loop is unrolled
-    // by six to name every buffer and register set statically.
-    TileScales sc0, sc1, sc2;
-    issue_tile(st0, t0, sc0);
-    sc2 = sc1 = sc0;
-    if (ntiles > 1) issue_tile(st1, t0 + 1, sc1);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    f32x16 sa[NB_C], sb[NB_C];
-    if (wave_needs(0)) gemm1(st0, sc0, sa);
-    auto step = [&](int j, char* cur, char* nxt, char* fut, const TileScales& scc, const TileScales& scn,
-                    TileScales& scf, f32x16* s_cur, f32x16* s_nxt) {
-      if (j + 2 < ntiles) issue_tile(fut, t0 + j + 2, scf);
-      if (j + 1 < ntiles && wave_needs(j + 1)) gemm1(nxt, scn, s_nxt);
-      if (wave_needs(j)) softmax_gemm2(cur, j, scc, s_cur);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-    };
-    for (int j = 0;; j += 6) {
-      step(j, st0, st1, st2, sc0, sc1, sc2, sa, sb);
-      if (j + 1 >= ntiles) break;
-      step(j + 1, st1, st2, st0, sc1, sc2, sc0, sb, sa);
-      if (j + 2 >= ntiles) break;
-      step(j + 2, st2, st0, st1, sc2, sc0, sc1, sa, sb);
-      if (j + 3 >= ntiles) break;
-      step(j + 3, st0, st1, st2, sc0, sc1, sc2, sb, sa);
-      if (j + 4 >= ntiles) break;
-      step(j + 4, st1, st2, st0, sc1, sc2, sc0, sa, sb);
-      if (j + 5 >= ntiles) break;
-      step(j + 5, st2, st0, st1, sc2, sc0, sc1, sb, sa);
-      if (j + 6 >= ntiles) break;
-    }
-  } else {
-    // Ping-pong.  Every wave runs the phases M_0 V_0 M_1 V_1 ... M_J (J tiles): M_j multiplies
-    // P_{j-1} by V_{j-1} (second product of the previous tile) and forms S_j = K_j Q^T; V_j takes
-    // the softmax of S_j into the packed P_j.  A barrier ends every phase.  The second half of
-    // the workgroup (waves 4..7) passes one extra barrier at the start, so it runs one phase
-    // behind the first: while one wave of a SIMD multiplies, the other takes exponentials.
-    // Tile j lives in kb[j % 3] and vb[j % 3].  In its phase V_j the first half copies K_{j+2}
-    // and the second half copies V_{j+1}; both buffers were last read in the phases M_{j-1}.
-    // Each wave waits for its own copies at the end of its next M phase, and the barrier that
-    // follows publishes them; both tiles are first read in the first half's M_{j+2}.  Each wave
-    // loads the scales of tile j+2 in V_j into slot (j+2) % 3 (tile j-1's, whose last use was in
-    // M_j); the wait at the end of M_{j+1} covers them.
-    constexpr int HW = WAVES / 2;
-    constexpr int NIB = TILE / 1024 / HW;  // 1 KB copies per wave per tile
-    static_assert(NIB * HW * 1024 == TILE, "copy split");
-    const bool second = wave >= HW;
-    const int wb = wave % HW;
-    int voffb[NIB];
-#pragma unroll
-    for (int i = 0; i < NIB; ++i) {
-      int row, chunk;
-      f8_tile_row_chunk((wb * NIB + i) * 64 + lane, row, chunk);
-      voffb[i] = row * rowbytes + chunk * 16;
-    }
-    auto copy = [&](const char* base, char* dst, int j) {  // this wave's part of loop tile j
-      const int off = (t0 + j) * BC * rowbytes;
-      // the address is uniform; readfirstlane keeps the buffer resource in scalar registers
-      const uint64_t p = reinterpret_cast<uint64_t>(base + off);
-      const uint64_t pu = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(p >> 32)) << 32 |
-                          (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)p);
-      copy_rows_to_lds8<NIB>(reinterpret_cast<const char*>(pu), __builtin_amdgcn_readfirstlane(nbytes - off),
-                             dst + wb * NIB * 1024, voffb);
-    };
-    auto load_scales = [&](int j, TileScales& sc) {
-      const int blk = min((t0 + j) * (BC / 64), nblk - 1);
-      sc.k[0] = ksc[blk];
-      sc.v[0] = vsc[blk];
-    };
-    // loop tiles jlo .. jw-1 hold keys this wave sees (causal: up to its diagonal, and from its
-    // first query's window on)
-    const int jw = CAUSAL ? min(ntiles, (qw + 31) / BC + 1 - t0) : ntiles;
-    const int jlo = WINDOW ? max(0, qw - window + 1) / BC - t0 : 0;
-    f32x16 s[NB_C];
-    i32x8 pf[KS];
-    // M phase: the second product of tile j-1 (V^T operands, four transpose reads each), then
-    // the first product of tile j (K operands, two 16-byte reads each); every operand is read
-    // PD products ahead of its matrix instruction
-    constexpr int N2 = 4, N1 = 2 * NB_C, PD = 3;
-    auto operand = [&](const char* kt, const char* vt, int i) -> i32x8 {
-      if (i < N2) return v_operand(vt, 0, i);
-      const int cb = (i - N2) >> 1, st = (i - N2) & 1;
-      const u32x4 a0 = *reinterpret_cast<const u32x4*>(kt + koff[0] + cb * 4096 + st * 1024);
-      const u32x4 a1 = *reinterpret_cast<const u32x4*>(kt + koff[1] + cb * 4096 + st * 1024);
-      return i32x8{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
-    };
-    // Every M phase from this wave's first tile to its last runs the whole stream: in M_jlo P is
-    // still zero and the V buffer holds finite codes (in M_0 a copy of V_0), so the second
-    // product adds exact zeros; in M_jw the first product is formed and not used.  (One branch
-    // around the whole phase: branches around single products make the register allocator
-    // split the accumulators and spill.)
-    auto mphase = [&](const char* kt, const char* vt, int j, const TileScales& sck, const TileScales& scv) {
-      if (j >= jlo && j <= jw) {
-        const int sv = e8m0_of(scv.v[0]);
-        const int sk0 = e8m0_of(sck.k[0]);
-        i32x8 win[PD];
-#pragma unroll
-        for (int i = 0; i < PD; ++i) win[i] = operand(kt, vt, i);
-#pragma unroll
-        for (int i = 0; i < N2 + N1; ++i) {
-          const i32x8 a = win[i % PD];
-          if (i + PD < N2 + N1) win[i % PD] = operand(kt, vt, i + PD);
-          if (i < N2) {
-            oacc[i] = mma_f8(a, pf[0], oacc[i], sv, 127);
-          } else {
-            const int cb = (i - N2) >> 1, st = (i - N2) & 1;
-            s[cb] = mma_f8(a, qf[st], st == 0 ? f32x16{} : s[cb], sk0, sq);
-          }
-        }
-        // keep that order through instruction scheduling: the reads of the first PD operands,
-        // then per product: the product, the reads of the operand PD places ahead
-        auto reads = [](int i) {
-          if (i < N2) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-          else __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        };
-#pragma unroll
-        for (int i = 0; i < PD; ++i) reads(i);
-#pragma unroll
-        for (int i = 0; i < N2 + N1; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (i + PD < N2 + N1) reads(i + PD);
-        }
-      }
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's copies and scale loads (issued in its last V phase) have landed
-    };
-    auto vphase = [&](char* kdst, char* vdst, int j, TileScales& scn) {
-      if (j + 2 < ntiles) load_scales(j + 2, scn);
-      if (!second) {
-        if (j + 2 < ntiles) copy(kbase, kdst, j + 2);
-      } else {
-        if (j + 1 < ntiles) copy(vbase, vdst, j + 1);
-      }
-      if (j >= jlo && j < jw) softmax(j, s, pf);
-    };
-    TileScales sc0, sc1, sc2;
-    load_scales(0, sc0);
-    sc2 = sc1 = sc0;
-    if (ntiles > 1) load_scales(1, sc1);
-    pf[0] = i32x8{};
-    if (!second) {
-      copy(kbase, kb0, 0);
-      if (ntiles > 1) copy(kbase, kb1, 1);
-    } else {
-      copy(vbase, vb0, 0);
-      copy(vbase, vb2, 0);  // read (times P = 0) by M_0
-    }
-    __builtin_amdgcn_s_waitcnt(0);  // tiles K_0, K_1, V_0 and the scales of tiles 0 and 1 have arrived
-    __syncthreads();
-    if (second) phase_barrier8();
-    for (int j = 0;; j += 3) {
-      mphase(kb0, vb2, j, sc0, sc2);
-      phase_barrier8();
-      if (j == ntiles) break;
-      vphase(kb2, vb1, j, sc2);
-      phase_barrier8();
-      mphase(kb1, vb0, j + 1, sc1, sc0);
-      phase_barrier8();
-      if (j + 1 == ntiles) break;
-      vphase(kb0, vb2, j + 1, sc0);
-      phase_barrier8();
-      mphase(kb2, vb1, j + 2, sc2, sc1);
-      phase_barrier8();
-      if (j + 2 == ntiles) break;
-      vphase(kb1, vb0, j + 2, sc1);
-      phase_barrier8();
-    }
-    // the first half passes one barrier fewer in the loop; it joins the second half's last
-    // barrier after its epilogue (below)
   }
 
   const float lt = halves_sum(l);
@@ -819,13 +622,10 @@ __global__ __launch_bounds__(64 * WAVES, (WAVES == 4 ? (LOOP == kLoopTwoStage ? 
       lse[idx] = lt > 0.f ? m * alpha + __logf(lt) - (float)kPExp * kLn2 : -INFINITY;
     }
   }
-  if constexpr (PP) {
-    if (wave < WAVES / 2) phase_barrier8();
-  }
 }
 
 #ifndef ATTN_FP8_SHAPE
-#define ATTN_FP8_SHAPE 4, 64, kLoopOne
+#define ATTN_FP8_SHAPE 4, 64
 #endif
 
 }  // namespace

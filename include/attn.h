@@ -21,8 +21,12 @@
  *     nothing and keeps no state between calls, so calls are thread-safe.
  *   - Work is enqueued on `stream` (NULL = the default stream) and the call returns without
  *     synchronising.  Faults of the enqueued kernels surface at the caller's next sync.
- *   - Every argument is validated before anything is enqueued; a non-zero status means
- *     nothing was launched.  attn_strerror() names a status.
+ *   - Every argument is validated before anything is enqueued: ATTN_ERR_INVALID,
+ *     ATTN_ERR_UNSUPPORTED and ATTN_ERR_ALIGN mean nothing was launched.  ATTN_ERR_HIP means
+ *     the HIP runtime refused a launch; an entry point that enqueues several kernels (the
+ *     backward pass, per-tensor FP8 scaling) may already have enqueued the ones before it.
+ *     An error left pending by earlier, unrelated HIP work is cleared before the first
+ *     launch, so it is not reported here.  attn_strerror() names a status.
  *   - Tensors are contiguous with the head dimension innermost (d contiguous), and every
  *     q/k/v/o pointer must be 16-byte aligned (misaligned or strided views are the silent-
  *     wrong-result pitfall named in the blog article's deployment section, so they are

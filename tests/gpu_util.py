@@ -33,13 +33,31 @@ def to_device(inp: seeded_inputs.AttnInputs):
     return q, k, v, cu
 
 
-def run_gpu(inp: seeded_inputs.AttnInputs):
-    """libattn forward on the device; returns float64 numpy O (input layout) and LSE."""
+def attention_nan(q, k, v, *, causal=False, alpha=None, cu_seqlens=None, max_seqlen=None, window=None,
+                  q_scale=None, k_scale=None, v_scale=None):
+    """attn_fwd (or attn_fwd_window) into O and LSE pre-filled with NaN: a row that no workgroup
+    writes stays NaN, so the tests' finiteness checks prove that every row was written."""
     import exact_attention_76_amd as ea
 
+    out_dtype = torch.float16 if q.dtype == torch.float16 else torch.bfloat16
+    o = torch.full(q.shape, float("nan"), dtype=out_dtype, device=q.device)
+    lse_shape = (q.shape[0], q.shape[2], q.shape[1]) if cu_seqlens is None else (q.shape[1], q.shape[0])
+    lse = torch.full(lse_shape, float("nan"), dtype=torch.float32, device=q.device)
+    torch.cuda.synchronize()
+    kw = dict(alpha=alpha, cu_seqlens=cu_seqlens, max_seqlen=max_seqlen, q_scale=q_scale, k_scale=k_scale,
+              v_scale=v_scale)
+    if window:
+        ea.attn_fwd_window(q, k, v, o, lse, window=window, **kw)
+    else:
+        ea.attn_fwd(q, k, v, o, lse, causal=causal, **kw)
+    return o, lse
+
+
+def run_gpu(inp: seeded_inputs.AttnInputs):
+    """libattn forward on the device; returns float64 numpy O (input layout) and LSE."""
     q, k, v, cu = to_device(inp)
-    o, lse = ea.attention(q, k, v, causal=inp.causal, alpha=inp.alpha, cu_seqlens=cu,
-                          max_seqlen=inp.N if cu is not None else None, window=inp.window or None)
+    o, lse = attention_nan(q, k, v, causal=inp.causal, alpha=inp.alpha, cu_seqlens=cu,
+                           max_seqlen=inp.N if cu is not None else None, window=inp.window or None)
     torch.cuda.synchronize()
     return o.double().cpu().numpy(), lse.double().cpu().numpy()
 
@@ -64,6 +82,28 @@ def sample_rows(inp, n: int, seed: int = 0):
     tokens = np.concatenate(toks)
     heads = rng.integers(0, inp.Hq, len(tokens))
     return heads, tokens
+
+
+def coverage_rows(inp, br: int, whole_heads=None, seed: int = 0):
+    """Rows (head, packed token) that cover a full-size launch: one query drawn from every
+    (sequence, head, query block of br queries) -- so every workgroup of the grid has at least
+    one checked row -- plus every token of the heads in ``whole_heads`` (default: the first and
+    the last head, which sit on different XCDs and, with grouped heads, different KV groups)."""
+    rng = np.random.default_rng(seed)
+    cu = inp.cu_seqlens.astype(np.int64) if inp.cu_seqlens is not None else np.arange(inp.B + 1) * inp.N
+    whole = (0, inp.Hq - 1) if whole_heads is None else whole_heads
+    heads, tokens = [], []
+    for b in range(len(cu) - 1):
+        n = int(cu[b + 1] - cu[b])
+        for q0 in range(0, n, br):
+            cnt = min(br, n - q0)
+            heads.append(np.arange(inp.Hq))
+            tokens.append(cu[b] + q0 + rng.integers(0, cnt, inp.Hq))
+    T = int(cu[-1])
+    for h in whole:
+        heads.append(np.full(T, h))
+        tokens.append(np.arange(T))
+    return np.concatenate(heads).astype(np.int64), np.concatenate(tokens).astype(np.int64)
 
 
 def gpu_rows(inp, o_gpu, lse_gpu, heads, tokens):

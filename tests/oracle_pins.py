@@ -279,6 +279,30 @@ def pin_invariants(lib):
     _close(ld.transpose(1, 0, 2).reshape(Hq, 15), lv, 0.0, "dense vs varlen L")
 
 
+def pin_empty_sequences(lib):
+    """Zero-length sequences anywhere in a pack (first, middle, last, and two in a row) own no
+    tokens: every token still belongs to the sequence that holds it, so the packed result equals
+    independent runs of the non-empty sequences, through both entry points."""
+    Hq, Hkv, d = 4, 2, 6
+    lengths = [0, 4, 0, 0, 1, 7, 0]
+    cu = np.concatenate([[0], np.cumsum(lengths)])
+    T = int(cu[-1])
+    q, k, v = _rand((T, Hq, d), 90), _rand((T, Hkv, d), 91), _rand((T, Hkv, d), 92)
+    for causal in (False, True):
+        o, lse = lib.attention(q, k, v, causal=causal, cu_seqlens=cu)
+        for s in range(len(lengths)):
+            a0, a1 = cu[s], cu[s + 1]
+            if a1 == a0:
+                continue
+            os_, ls_ = lib.attention(q[None, a0:a1], k[None, a0:a1], v[None, a0:a1], causal=causal)
+            _close(o[a0:a1], os_[0], 0.0, "packed with empty sequences vs per-sequence O")
+            _close(lse[:, a0:a1], ls_[0], 0.0, "packed with empty sequences vs per-sequence L")
+        hs, ts = np.repeat(np.arange(Hq), T), np.tile(np.arange(T), Hq)
+        orow, lrow = lib.attention_rows(q, k, v, hs, ts, causal=causal, cu_seqlens=cu)
+        _close(orow, o[ts, hs], 0.0, "rows with empty sequences O")
+        _close(lrow, lse[hs, ts], 0.0, "rows with empty sequences L")
+
+
 def pin_rows_match_full(lib):
     """The sampled-row entry point returns exactly the rows of the full computation."""
     cu = np.array([0, 9, 30, 31])
@@ -391,5 +415,5 @@ def pin_sliding_window(lib):
 
 
 ALL_PINS = [pin_causal_first_row, pin_uniform_scores, pin_one_hot_key, pin_golden_weights,
-            pin_bruteforce_mpmath, pin_torch_sdpa, pin_invariants, pin_rows_match_full,
+            pin_bruteforce_mpmath, pin_torch_sdpa, pin_invariants, pin_empty_sequences, pin_rows_match_full,
             pin_algorithm1, pin_sliding_window]

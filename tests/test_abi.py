@@ -187,3 +187,29 @@ def test_bwd_window_validation(lib, window, status):
     P = ctypes.c_void_p
     assert lib.attn_bwd_window(P(A), P(A), P(A), P(A), P(A), P(A), P(A), P(A), P(A), P(A), 1, 2, 2, 128, None, 128,
                                window, 0.125, ea.ATTN_BF16, None) == status
+
+
+def test_library_matches_sources_on_disk():
+    """build() records the sha256 of every source beside libattn.so; the record must match the
+    tree (the loaded library is the committed code)."""
+    ea.check_build_record()
+
+
+def test_stale_library_is_refused(tmp_path, monkeypatch):
+    import json
+
+    from exact_attention_76_amd import build as b
+
+    rec = json.load(open(b.RECORD))
+    name = sorted(rec["sources"])[0]
+    rec["sources"][name] = "0" * 64
+    stale = tmp_path / "record.json"
+    stale.write_text(json.dumps(rec))
+    monkeypatch.setattr(b, "RECORD", str(stale))
+    with pytest.raises(OSError, match="not built from the sources on disk"):
+        ea.check_build_record()
+    rec["sources"][name] = b.source_record()["sources"][name]
+    rec["extra_flags"] = "-DATTN_D128_SHAPE=64,attn::LoopShape<8>"
+    stale.write_text(json.dumps(rec))
+    with pytest.raises(OSError, match="compiler arguments"):
+        ea.check_build_record()

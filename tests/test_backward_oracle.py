@@ -112,7 +112,28 @@ def pin_magnitudes_bound(mod):
         assert np.all(np.abs(x) <= y * (1 + 1e-12) + 1e-15)
 
 
-ALL_PINS = [pin_finite_differences, pin_torch_autograd, pin_invariants, pin_magnitudes_bound]
+def pin_magnitudes_tight(mod):
+    """The magnitude sums are exactly the gradients' sizes when every term of a sum has one sign,
+    so an inflated bound (which would loosen every backward tolerance) fails here.  Two keys with
+    K_1 = -K_0 make each term of dQ = alpha (dS_i0 K_0 + dS_i1 K_1) share a sign (dS_i1 = -dS_i0);
+    two identical query rows (and dO rows) make the terms of dK_j = alpha sum_i dS_ij Q_i equal;
+    dO >= 0 makes every term of dV = P^T dO non-negative."""
+    B, N, H, d = 1, 2, 1, 4
+    q1 = _rand((d,), 21)
+    q = np.stack([q1, q1])[None, :, None, :]
+    k0 = _rand((d,), 22)
+    k = np.stack([k0, -k0])[None, :, None, :]
+    v = _rand((B, N, H, d), 23)
+    do1 = np.abs(_rand((d,), 24)) + 0.1
+    do = np.stack([do1, do1])[None, :, None, :]
+    g = mod.attention_backward(q, k, v, do, causal=False, alpha=0.4)
+    m = mod.gradient_magnitudes(q, k, v, do, causal=False, alpha=0.4)
+    for name, x, y in zip(("dQ", "dK", "dV"), g, m):
+        assert np.max(np.abs(x)) > 1e-3, f"{name}: degenerate case"
+        assert np.allclose(np.abs(x), y, rtol=1e-12, atol=1e-15), f"{name}: magnitude sum is not tight"
+
+
+ALL_PINS = [pin_finite_differences, pin_torch_autograd, pin_invariants, pin_magnitudes_bound, pin_magnitudes_tight]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
@@ -126,6 +147,10 @@ MUTATIONS = {
     "dv_from_unnormalised": ("dv[:, g, :] += P.T @ dO", "dv[:, g, :] += E.T @ dO"),
     "dk_overwrites_group": ("dk[:, g, :] += alpha * (dS.T @ Q)", "dk[:, g, :] = alpha * (dS.T @ Q)"),
     "dP_from_keys": ("            dP = dO @ V.T\n            D =", "            dP = dO @ K.T\n            D ="),
+    "magnitudes_triangle": ("dS = np.abs(P * (dP - np.sum(P * dP, axis=1, keepdims=True)))",
+                            "dS = P * (np.abs(dP) + np.abs(np.sum(P * dP, axis=1, keepdims=True)))"),
+    "magnitudes_without_alpha": ("mq[rows, h, :] = alpha * (dS @ np.abs(K))", "mq[rows, h, :] = dS @ np.abs(K)"),
+    "magnitudes_dv_unnormalised": ("mv[:, g, :] += P.T @ np.abs(dO)", "mv[:, g, :] += E.T @ np.abs(dO)"),
     "window_off_by_one": ("    if window > 0:\n        vis &= j > i[:, None] - window",
                        "    if window > 0:\n        vis &= j > i[:, None] - window - 1"),
 }

@@ -10,10 +10,11 @@
   rotary embedding (fp32 tables), dense and packed.
 * attn_fwd on e4m3 inputs -- dense and packed, causal or not, grouped-query heads -- against
   the fp64 oracle run on the *unquantised* bf16 inputs (the
-  error measure of the FlashAttention-3 digest's section 3.5 / Table 3): O RMSE <= 3e-2, or the
-  floor that quantising the inputs sets for any implementation (exact attention on the
-  dequantised inputs) plus 2e-3 where that floor is higher.  The kernel's own error (against
-  the oracle run on its dequantised inputs) is bounded separately.
+  error measure of the FlashAttention-3 digest's section 3.5 / Table 3): O RMSE <= 3e-2, or, for
+  the cases whose inputs alone already miss it, the floor pinned on the CPU from the oracle
+  (tests/golden/fp8_quantisation_floors.txt) plus 2e-3.  The kernel's own error (against the
+  oracle run on its dequantised inputs) is bounded separately, at full size on one row of every
+  workgroup and two whole heads.
 """
 import numpy as np
 import pytest
@@ -22,6 +23,7 @@ import torch
 import oracle
 import seeded_inputs as si
 from oracle import fp8 as ofp8
+from tests import fp8_cases
 from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
@@ -135,13 +137,20 @@ def test_prepare_scale_floor_and_zero_blocks(per_tensor, rotate):
 
 
 def gpu_fp8_attention(inp, signs, per_tensor=False):
-    import exact_attention_76_amd as ea
-
+    """Pre-pass and attention on the device; O and LSE start as NaN (every row must be written)."""
     q8, k8, v8, qs, ks, vs = gpu_prepare(inp, signs, per_tensor)
-    o, lse = ea.attention(q8, k8, v8, causal=inp.causal, alpha=inp.alpha, q_scale=qs, k_scale=ks, v_scale=vs,
-                          window=inp.window or None, **_packed(inp))
+    o, lse = gu.attention_nan(q8, k8, v8, causal=inp.causal, alpha=inp.alpha, q_scale=qs, k_scale=ks, v_scale=vs,
+                              window=inp.window or None, **_packed(inp))
     torch.cuda.synchronize()
     return o.double().cpu().numpy(), lse.double().cpu().numpy(), (q8, k8, v8, qs, ks, vs)
+
+
+def _dequantised(inp, prep):
+    q8, k8, v8, qs, ks, vs = (t.cpu().numpy() for t in prep)
+    cu = inp.cu_seqlens
+    if cu is None:
+        return ofp8.dequantize(q8, qs), ofp8.dequantize(k8, ks), ofp8.dequantize(v8, vs)
+    return tuple(ofp8.dequantize_varlen(c, sc, cu) for c, sc in ((q8, qs), (k8, ks), (v8, vs)))
 
 
 def _three_errors(inp, o, lse, prep, heads, tokens):
@@ -149,14 +158,9 @@ def _three_errors(inp, o, lse, prep, heads, tokens):
     dequantised inputs vs the same (Y, the floor the input quantisation sets for any
     implementation), and kernel vs exact attention on its own dequantised inputs (Z, the
     kernel's own error: P rounded to e4m3 and fp32 arithmetic)."""
-    q8, k8, v8, qs, ks, vs = (t.cpu().numpy() for t in prep)
-    cu = inp.cu_seqlens
-    if cu is None:
-        qd, kd, vd = ofp8.dequantize(q8, qs), ofp8.dequantize(k8, ks), ofp8.dequantize(v8, vs)
-    else:
-        qd, kd, vd = (ofp8.dequantize_varlen(c, sc, cu) for c, sc in ((q8, qs), (k8, ks), (v8, vs)))
+    qd, kd, vd = _dequantised(inp, prep)
     q, k, v = gu.widened(inp)
-    kw = dict(causal=inp.causal, alpha=inp.alpha, cu_seqlens=cu, window=inp.window)
+    kw = dict(causal=inp.causal, alpha=inp.alpha, cu_seqlens=inp.cu_seqlens, window=inp.window)
     o_ref, lse_ref = oracle.attention_rows(q, k, v, heads, tokens, **kw)
     o_dq, lse_dq = oracle.attention_rows(qd, kd, vd, heads, tokens, **kw)
     o_s, lse_s = gu.gpu_rows(inp, o, lse, heads, tokens)
@@ -167,6 +171,17 @@ def _three_errors(inp, o, lse, prep, heads, tokens):
     gu.say("fp8 quantised-input floor vs fp64", Y)
     gu.say("fp8 kernel vs dequantised-input oracle", Z)
     return X, Y, Z, lse_dq
+
+
+def _own_error(inp, o, lse, prep, heads, tokens):
+    """Z alone (kernel vs exact attention on its own dequantised inputs) on the given rows."""
+    qd, kd, vd = _dequantised(inp, prep)
+    kw = dict(causal=inp.causal, alpha=inp.alpha, cu_seqlens=inp.cu_seqlens, window=inp.window)
+    o_dq, lse_dq = oracle.attention_rows(qd, kd, vd, heads, tokens, **kw)
+    o_s, lse_s = gu.gpu_rows(inp, o, lse, heads, tokens)
+    Z = oracle.error_metrics(o_s, o_dq, lse_s, lse_dq)
+    gu.say("fp8 kernel vs dequantised-input oracle, coverage rows", len(heads), Z)
+    return Z, lse_dq
 
 
 # Kernel's own error budget (Z): P is rounded to e4m3 (relative step 2^-3, so at most 2^-4 per
@@ -183,50 +198,73 @@ def own_lse_bound(lse_dq):
     return max(gu.TOL_LSE, 2.0 ** -12 * float(np.max(np.abs(lse_dq))))
 
 
-def check_fp8(X, Y, Z, lse_dq):
-    """X: kernel vs fp64; Y: input-quantisation floor vs fp64; Z: kernel vs dequantised oracle.
-    The bar is RMSE <= 3e-2 against fp64 on the unquantised inputs; where quantising the inputs
-    alone (Y) already costs more than that, no implementation can meet it, and the kernel is
-    held to Y plus 2e-3 instead."""
+FLOORS = fp8_cases.stored_floors()
+
+
+def check_own(Z, lse_dq):
     assert Z["rmse"] <= TOL_FP8_OWN_RMSE, Z
     assert Z["lse_max_abs"] <= own_lse_bound(lse_dq), (Z, own_lse_bound(lse_dq))
-    assert X["rmse"] <= max(gu.TOL_FP8_RMSE, Y["rmse"] + 2e-3), (X, Y)
+
+
+def check_fp8(X, Y, Z, lse_dq, floor=None):
+    """X: kernel vs fp64; Y: input-quantisation floor vs fp64; Z: kernel vs dequantised oracle.
+    The bar is RMSE <= 3e-2 against fp64 on the unquantised inputs.  ``floor`` names a case of
+    tests/fp8_cases.py whose inputs alone already miss that bar: its floor is pinned on the CPU
+    from the oracle (tests/golden/fp8_quantisation_floors.txt), Y must reproduce it (the GPU
+    pre-pass codes are the oracle's), and the kernel is held to it plus 2e-3."""
+    check_own(Z, lse_dq)
+    if floor is None:
+        assert X["rmse"] <= gu.TOL_FP8_RMSE, (X, Y)
+        return
+    pinned = FLOORS[floor]
+    assert Y["rmse"] == pytest.approx(pinned, rel=1e-9), (floor, Y, pinned)
+    assert X["rmse"] <= pinned + 2e-3, (floor, X, pinned)
 
 
 @pytest.mark.parametrize("rotate", [True, False])
 def test_fp8_attention_small(rotate):
-    inp = si.fp8_inputs(2, 300, 4, 128, seed=601, fraction=0.002)
-    signs = si.hadamard_signs(128, seed=55) if rotate else None
+    """Small inputs with an x20 outlier channel, every row: the quantisation floor of these
+    inputs is above the bar (pinned floors small_rotated / small_unrotated)."""
+    name = "small_rotated" if rotate else "small_unrotated"
+    inp, signs, heads, tokens = fp8_cases.case(name)
     gu.say("fp8 attention small", rotate)
     o, lse, prep = gpu_fp8_attention(inp, signs)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
-    T = inp.B * inp.N
-    heads, tokens = np.repeat(np.arange(inp.Hq), T), np.tile(np.arange(T), inp.Hq)  # every row
-    check_fp8(*_three_errors(inp, o, lse, prep, heads, tokens))
+    check_fp8(*_three_errors(inp, o, lse, prep, heads, tokens), floor=name)
 
 
-def _full(inp, rows):
+BR8 = 128  # queries per workgroup of the FP8 attention kernel
+
+
+def _full(inp, floor=None, heads=None, tokens=None):
+    """Full-size FP8 attention in the benchmark's launch configuration: every row written (O and
+    LSE start as NaN), the kernel's own error on one row of every (sequence, head, query block)
+    -- every workgroup -- and on two whole heads, and the bar against fp64 on the unquantised
+    inputs over sampled rows (the first and last token of every sequence among them)."""
     signs = si.hadamard_signs(128, seed=55)
     o, lse, prep = gpu_fp8_attention(inp, signs)
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
-    heads, tokens = gu.sample_rows(inp, rows, seed=2)
-    return _three_errors(inp, o, lse, prep, heads, tokens)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), "rows left unwritten"
+    check_own(*_own_error(inp, o, lse, prep, *gu.coverage_rows(inp, BR8, seed=3)))
+    if heads is None:
+        heads, tokens = fp8_cases.sample_rows(inp, 2048, seed=2)
+    check_fp8(*_three_errors(inp, o, lse, prep, heads, tokens), floor=floor)
 
 
 def test_fp8_attention_full_workload():
-    """B=2, H=16, N=8192, d=128 with two x20 outlier channels shared by Q, K and V."""
-    inp = si.CONFIGS["fp8_b2_h16_n8192_d128"]()
+    """B=2, H=16, N=8192, d=128 with two x20 outlier channels shared by Q, K and V.  On this
+    reading the inputs' quantisation floor (0.0357, pinned on the CPU) is above the 3e-2 bar:
+    the kernel is held to that floor plus 2e-3."""
+    inp, _, heads, tokens = fp8_cases.case("c5_shared_channels")
     gu.say("fp8 attention full workload")
-    check_fp8(*_full(inp, 2048))
+    _full(inp, floor="c5_shared_channels", heads=heads, tokens=tokens)
 
 
 def test_fp8_attention_full_workload_independent_outliers():
-    """The other reading of the outlier construction: independent channel draws for Q, K, V."""
+    """The other reading of the outlier construction: independent channel draws for Q, K, V.
+    Its floor is under the bar, so the kernel is held to 3e-2 itself."""
     inp = si.fp8_inputs(2, 8192, 16, 128, seed=5, independent_channels=True)
     gu.say("fp8 attention full workload, independent outlier channels")
-    X, Y, Z, lse_dq = _full(inp, 2048)
-    check_fp8(X, Y, Z, lse_dq)
-    assert X["rmse"] <= gu.TOL_FP8_RMSE, X
+    _full(inp)
 
 
 # ---- packed sequences, causal masks, grouped-query heads ----------------------------------------
@@ -298,18 +336,18 @@ def test_fp8_attention_causal_row0_is_v0():
 
 
 def test_fp8_attention_full_causal():
-    """B=2, H=16, N=8192, d=128, causal, sampled rows."""
+    """B=2, H=16, N=8192, d=128, causal."""
     inp = si.dense_inputs(2, 8192, 16, 128, causal=True, seed=614)
     gu.say("fp8 attention full causal")
-    check_fp8(*_full(inp, 2048))
+    _full(inp)
 
 
 def test_fp8_attention_full_varlen_gqa():
     """The packed workload's shape: 8 sequences of 256 .. 8192 tokens, 32 query heads on 8 KV
-    heads, causal, sampled rows (the first and last token of every sequence among them)."""
+    heads, causal."""
     inp = si.CONFIGS["gqa_varlen_causal_hq32_hkv8_d128"]()
     gu.say("fp8 attention full packed GQA causal")
-    check_fp8(*_full(inp, 2048))
+    _full(inp)
 
 
 # ---- pre-pass fused with the rotary embedding ----------------------------------------------------

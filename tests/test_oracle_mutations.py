@@ -30,6 +30,9 @@ MUTATIONS = {
                             "const double* qrow = q + (t * Hq + g) * d;"),
     "sequence_end_ignored": ("const int64_t n = cu[b + 1] - start;", "const int64_t n = cu[nseq] - start;"),
     "window_off_by_one": ("const int64_t lo = i - window + 1;", "const int64_t lo = i - window;"),
+    "sequence_search_takes_first_of_equal_offsets": (
+        "    if (cu[mid] <= t) lo = mid; else hi = mid - 1;\n  }\n  return lo;",
+        "    if (cu[mid] <= t) lo = mid; else hi = mid - 1;\n  }\n  while (lo > 0 && cu[lo - 1] == cu[lo]) --lo;\n  return lo;"),
     "window_ignored": ("const int64_t first = (window > 0 && lo > 0) ? lo : 0;", "const int64_t first = 0;"),
     "window_from_sequence_start": ("const int64_t first = (window > 0 && lo > 0) ? lo : 0;",
                                    "const int64_t first = (window > 0 && lo > 0) ? lo - (int64_t)(start > 0) : 0;"),
