@@ -11,6 +11,8 @@ Entry points carry the names of the C ABI:
 * :func:`attn_fwd_window` -- the same, causal, inside a sliding window of W keys.
 * :func:`attn_bwd` -- dQ, dK, dV of attn_fwd's output (16-bit inputs); with ``window`` it calls
   ``attn_bwd_window`` (the C entry point of the same name).
+* :func:`attn_bwd_noalloc` -- attn_bwd without a workspace argument, for callers that cannot
+  allocate device memory (the library's static per-GPU workspace).
 * :func:`attn_fp8_prepare` -- Hadamard rotation + per-block power-of-two e4m3 quantisation.
 * :func:`attn_fp8_prepare_ex` -- the same for packed sequences too, with per-block or per-tensor
   scales.
@@ -27,7 +29,8 @@ import re
 
 import torch
 
-__all__ = ["AttnError", "attn_fwd", "attn_fwd_window", "attn_bwd", "attn_bwd_window", "attention_backward", "attn_fp8_prepare", "attn_fp8_prepare_ex", "attn_strerror", "attention",
+__all__ = ["AttnError", "attn_fwd", "attn_fwd_window", "attn_bwd", "attn_bwd_window", "attn_bwd_noalloc",
+           "attention_backward", "attn_fp8_prepare", "attn_fp8_prepare_ex", "attn_strerror", "attention",
            "fp8_prepare", "load_library", "LIB_PATH", "ATTN_BF16", "ATTN_FP16", "ATTN_FP8_E4M3",
            "ATTN_FP8_SCALE_BLOCK", "ATTN_FP8_SCALE_TENSOR"]
 
@@ -37,6 +40,8 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "attn.h")
 
 ATTN_BF16, ATTN_FP16, ATTN_FP8_E4M3 = 0, 1, 2
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_ALIGN, ATTN_ERR_HIP = 0, -1, -2, -3, -4
+ATTN_ERR_TOO_LARGE = -5
+ATTN_BWD_NOALLOC_MAX_ROWS = 1 << 22
 ATTN_FP8_SCALE_BLOCK, ATTN_FP8_SCALE_TENSOR = 0, 1
 
 _lib = None
@@ -90,6 +95,8 @@ def load_library(build_if_missing: bool = True):
     lib.attn_bwd.restype = I
     lib.attn_bwd_window.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, P, I, I, F, I, P]
     lib.attn_bwd_window.restype = I
+    lib.attn_bwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, P, I, I, F, I, P]
+    lib.attn_bwd_noalloc.restype = I
     lib.attn_bwd_workspace_bytes.argtypes = [I, I, I]
     lib.attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.attn_fp8_prepare.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, P]
@@ -286,6 +293,27 @@ def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, *, causal: bool = Fal
             st = lib.attn_bwd(*args, int(bool(causal)), alpha_v, dt, _stream_handle(stream, dev))
     if st != ATTN_OK:
         raise AttnError(st, "attn_bwd_window" if window is not None else "attn_bwd")
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, *, causal: bool = False, alpha: float | None = None,
+                     cu_seqlens=None, max_seqlen: int | None = None, stream=None) -> None:
+    """Enqueue attn_bwd_noalloc: :func:`attn_bwd` without a workspace argument, for callers that
+    cannot allocate (D lives in the library's static per-GPU array of ATTN_BWD_NOALLOC_MAX_ROWS
+    floats; calls that overlap on one GPU race on it)."""
+    dev, head, tail = _fwd_call(q, k, v, o, lse, cu_seqlens, max_seqlen, None, None, None, alpha)
+    for name, t, ref in (("dout", dout, o), ("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _check_tensor(t, name)
+        if t.dtype != ref.dtype or tuple(t.shape) != tuple(ref.shape):
+            raise ValueError(f"{name} must match {tuple(ref.shape)} {ref.dtype}")
+    _one_device((("q", q), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)))
+    lib = load_library()
+    B, Hq, N = head[5], head[6], head[8]
+    with torch.cuda.device(dev):
+        st = lib.attn_bwd_noalloc(head[0], head[1], head[2], head[3], head[4], _ptr(dout), _ptr(dq), _ptr(dk),
+                                  _ptr(dv), B, Hq, head[7], N, head[9], head[10], int(bool(causal)), tail[0],
+                                  tail[1], _stream_handle(stream, dev))
+    if st != ATTN_OK:
+        raise AttnError(st, "attn_bwd_noalloc")
 
 
 def attention_backward(q, k, v, o, lse, dout, *, causal: bool = False, alpha: float | None = None, cu_seqlens=None,

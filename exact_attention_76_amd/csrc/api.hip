@@ -7,7 +7,38 @@
 #include "attn.h"
 #include "internal.h"
 
+#include <mutex>
+
+// Workspace of attn_bwd_noalloc: D = rowsum(dO * O) for up to ATTN_BWD_NOALLOC_MAX_ROWS rows.
+// Each GPU the library runs on holds its own copy of this array, at its own address, until the
+// process ends.  In host code its name is only a stand-in: the device address of each copy is
+// looked up once per device (scratch_on) and only that address is passed to kernels.
+static __device__ __align__(256) float scratch[ATTN_BWD_NOALLOC_MAX_ROWS];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+float* scratch_ptr[kMaxDevices] = {};
+
+// Device address of `dev`'s copy of scratch, looked up on the first use with that device
+// current (the caller's current device is restored).
+int scratch_on(int dev, float** out) {
+  if (dev < 0 || dev >= kMaxDevices) return ATTN_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return ATTN_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return ATTN_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) (void)hipSetDevice(cur);
+    if (err != hipSuccess || p == nullptr) return ATTN_ERR_HIP;
+    scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *out = scratch_ptr[dev];
+  return ATTN_OK;
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -69,10 +100,10 @@ int fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
   return status_of(err);
 }
 
-// attn_bwd and attn_bwd_window: window = 0 is no window.
-int bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
-        void* dk, void* dv, float* workspace, int B, int Hq, int Hkv, int N, const int* cu_seqlens, int d, int causal,
-        int window, float alpha, attn_dtype_t dtype, hipStream_t stream) {
+// Argument checks of the backward entry points (everything but the window).
+int bwd_validate(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                 void* dq, void* dk, void* dv, const float* workspace, int B, int Hq, int Hkv, int N, int d,
+                 int causal, float alpha, attn_dtype_t dtype) {
   int rc = validate_common(q, k, v, o, lse, B, Hq, Hkv, N);
   if (rc != ATTN_OK) return rc;
   if (!dout || !dq || !dk || !dv || !workspace) return ATTN_ERR_INVALID;
@@ -85,6 +116,15 @@ int bwd(const void* q, const void* k, const void* v, const void* o, const float*
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
       !aligned16(dk) || !aligned16(dv) || !aligned16(workspace))
     return ATTN_ERR_ALIGN;
+  return ATTN_OK;
+}
+
+// attn_bwd and attn_bwd_window: window = 0 is no window.
+int bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout, void* dq,
+        void* dk, void* dv, float* workspace, int B, int Hq, int Hkv, int N, const int* cu_seqlens, int d, int causal,
+        int window, float alpha, attn_dtype_t dtype, hipStream_t stream) {
+  const int rc = bwd_validate(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, d, causal, alpha, dtype);
+  if (rc != ATTN_OK) return rc;
   attn::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, cu_seqlens, d, causal, window, alpha};
   clear_pending_error();
   return status_of(attn::launch_bwd_16bit(a, dtype == ATTN_BF16, stream));
@@ -102,6 +142,8 @@ const char* attn_strerror(int status) {
     case ATTN_ERR_UNSUPPORTED: return "unsupported combination of head dim, dtype and mode";
     case ATTN_ERR_ALIGN: return "tensor pointer not 16-byte aligned";
     case ATTN_ERR_HIP: return "HIP runtime refused the launch";
+    case ATTN_ERR_TOO_LARGE: return "B * Hq * N exceeds the static workspace of attn_bwd_noalloc "
+                                    "(ATTN_BWD_NOALLOC_MAX_ROWS)";
     default: return "unknown status";
   }
 }
@@ -132,6 +174,24 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              int d, int causal, float alpha, attn_dtype_t dtype, hipStream_t stream) {
   return bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, B, Hq, Hkv, N, cu_seqlens, d, causal, 0, alpha, dtype,
              stream);
+}
+
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                     void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, const int* cu_seqlens, int d,
+                     int causal, float alpha, attn_dtype_t dtype, hipStream_t stream) {
+  if (B > 0 && Hq > 0 && N > 0 && (long long)B * Hq * N > ATTN_BWD_NOALLOC_MAX_ROWS) return ATTN_ERR_TOO_LARGE;
+  // every other argument is checked exactly as attn_bwd checks it before the workspace is
+  // looked up; a non-null stand-in passes the workspace check
+  float* const probe = reinterpret_cast<float*>(256);
+  int rc = bwd_validate(q, k, v, o, lse, dout, dq, dk, dv, probe, B, Hq, Hkv, N, d, causal, alpha, dtype);
+  if (rc != ATTN_OK) return rc;
+  int dev = -1;
+  if (stream != nullptr ? hipStreamGetDevice(stream, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess)
+    return ATTN_ERR_HIP;
+  float* ws = nullptr;
+  rc = scratch_on(dev, &ws);
+  if (rc != ATTN_OK) return rc;
+  return bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, B, Hq, Hkv, N, cu_seqlens, d, causal, 0, alpha, dtype, stream);
 }
 
 int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,

@@ -56,7 +56,9 @@ enum {
                                 FP8 without scales */
   ATTN_ERR_UNSUPPORTED = -2, /* head dim / dtype / mode combination without a kernel */
   ATTN_ERR_ALIGN = -3,       /* a tensor pointer is not 16-byte aligned */
-  ATTN_ERR_HIP = -4          /* the HIP runtime refused the launch */
+  ATTN_ERR_HIP = -4,         /* the HIP runtime refused the launch */
+  ATTN_ERR_TOO_LARGE = -5    /* attn_bwd_noalloc: the problem needs more than the library's
+                                static workspace holds */
 };
 
 /*
@@ -90,7 +92,7 @@ enum {
  * Limits: one head's K (or V) rows must span less than 2 GiB, i.e. N * Hkv * d * sizeof(element)
  * < 2^31 (ATTN_ERR_UNSUPPORTED otherwise); B * N < 2^31 tokens.
  *
- * Returns ATTN_OK or a negative status; on error nothing is enqueued.
+ * Returns ATTN_OK or a negative status; on a validation error nothing is enqueued.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int Hq, int Hkv, int N, const int* cu_seqlens,
@@ -132,8 +134,8 @@ int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float*
  *   the caller; on return it holds D in lse's layout.  Nothing is allocated.
  * d: 64 or 128; dtype: ATTN_BF16 or ATTN_FP16 (ATTN_ERR_UNSUPPORTED otherwise).
  * Limits: N * Hq * d * 2 < 2^31 (one head's q rows addressed with 32-bit offsets).
- * Three kernels run in order on `stream`.  Returns ATTN_OK or a negative status; on error
- * nothing is enqueued.
+ * Three kernels run in order on `stream`.  Returns ATTN_OK or a negative status (see the
+ * conventions at the top for what each means about enqueued work).
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
              const void* dout, void* dq, void* dk, void* dv, float* workspace,
@@ -153,6 +155,29 @@ int attn_bwd_window(const void* q, const void* k, const void* v, const void* o, 
 
 /* Bytes of workspace attn_bwd needs (B * Hq * N floats); 0 for non-positive sizes. */
 size_t attn_bwd_workspace_bytes(int B, int Hq, int N);
+
+/* Rows (B * Hq * N) the static workspace of attn_bwd_noalloc holds: 2^22 fp32 values, 16 MiB. */
+#define ATTN_BWD_NOALLOC_MAX_ROWS (1 << 22)
+
+/*
+ * attn_bwd_noalloc -- attn_bwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments, same
+ * kernels and bit-identical results as attn_bwd, without the workspace argument: D lives in a
+ * device array of ATTN_BWD_NOALLOC_MAX_ROWS floats that the library holds, one per GPU it runs
+ * on, for the life of the process.
+ *   - B * Hq * N must not exceed ATTN_BWD_NOALLOC_MAX_ROWS (ATTN_ERR_TOO_LARGE otherwise;
+ *     checked before anything else is looked up or enqueued).
+ *   - The device is that of `stream` (the current device for the NULL stream).  The first call
+ *     on a device looks up that device's copy of the array (hipGetSymbolAddress); no call
+ *     allocates device memory.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap on one GPU (different
+ *     streams or threads) race on it and give wrong gradients; serialise them.  Each call
+ *     writes every entry it reads first, so nothing needs clearing between calls.
+ */
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                     const void* dout, void* dq, void* dk, void* dv,
+                     int B, int Hq, int Hkv, int N, const int* cu_seqlens,
+                     int d, int causal, float alpha, attn_dtype_t dtype, hipStream_t stream);
 
 /*
  * attn_fp8_prepare -- the FP8 pre-pass (digest section 3.5: block quantisation and

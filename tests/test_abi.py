@@ -19,9 +19,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = ea.header_functions()
-    assert set(names) == {"attn_fwd", "attn_fwd_window", "attn_bwd", "attn_bwd_window", "attn_bwd_workspace_bytes",
-                          "attn_fp8_prepare",
-                          "attn_fp8_prepare_ex", "attn_strerror"}
+    assert set(names) == {"attn_fwd", "attn_fwd_window", "attn_bwd", "attn_bwd_window", "attn_bwd_noalloc",
+                          "attn_bwd_workspace_bytes", "attn_fp8_prepare", "attn_fp8_prepare_ex", "attn_strerror"}
     out = subprocess.run(["nm", "-D", "--defined-only", ea.LIB_PATH], capture_output=True, text=True,
                          check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
@@ -31,7 +30,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_strerror(lib):
-    for st in (0, -1, -2, -3, -4):
+    for st in (0, -1, -2, -3, -4, -5):
         assert ea.attn_strerror(st) and ea.attn_strerror(st) != "unknown status"
     assert ea.attn_strerror(7) == "unknown status"
 
@@ -213,3 +212,21 @@ def test_stale_library_is_refused(tmp_path, monkeypatch):
     stale.write_text(json.dumps(rec))
     with pytest.raises(OSError, match="compiler arguments"):
         ea.check_build_record()
+
+
+def test_noalloc_rejects_oversize_and_bad_arguments(lib):
+    """attn_bwd_noalloc checks the size against its static workspace, then every argument as
+    attn_bwd does, before it looks anything up on a device (so this runs without a GPU)."""
+    P = ctypes.c_void_p
+
+    def call(B=1, Hq=16, Hkv=16, N=128, d=64, dtype=ea.ATTN_BF16, q=A):
+        return lib.attn_bwd_noalloc(P(q), P(A), P(A), P(A), P(A), P(A), P(A), P(A), P(A), B, Hq, Hkv, N, None, d, 0,
+                                    0.125, dtype, None)
+
+    assert call(N=ea.ATTN_BWD_NOALLOC_MAX_ROWS // 16 + 1) == ea.ATTN_ERR_TOO_LARGE
+    assert call(B=3, Hq=32, Hkv=8, N=ea.ATTN_BWD_NOALLOC_MAX_ROWS // 96 + 1) == ea.ATTN_ERR_TOO_LARGE
+    assert call(q=0) == ea.ATTN_ERR_INVALID
+    assert call(Hq=6, Hkv=4) == ea.ATTN_ERR_INVALID
+    assert call(d=256) == ea.ATTN_ERR_UNSUPPORTED
+    assert call(dtype=ea.ATTN_FP8_E4M3) == ea.ATTN_ERR_UNSUPPORTED
+    assert call(q=A + 8) == ea.ATTN_ERR_ALIGN
