@@ -27,9 +27,18 @@ Each line carries
   roofline     -- algorithmic FLOPs per launch over the kernel's mean launch time, measured
                   with HIP events on the stream the kernel runs on, against the dtype's peak;
   cpu_baseline -- (headline only) the fp64 CPU oracle timed on a bounded sample of query rows
-                  of the same workload, as attention-FLOP throughput;
+                  of the same workload, as attention-FLOP throughput, on all host cores; with
+                  per_config (the same for every other workload) and one_core (the smallest
+                  workload and the N=4096 sweep point on one core);
 and, in config, the median and best single launch from a second pass of the same K launches
-with an event pair around each (after the timed region, so it does not perturb it).
+with an event pair around each (after the timed region, so it does not perturb it), and sclk:
+the graphics clock the power-management firmware reports while the same launch runs back to
+back for 2.5 s after the timed region, with the dense peak recomputed at that clock.
+
+The default line also carries, in config.workloads, every other workload timed the same way
+(the smallest one, the causal head dims, the packed causal GQA workload, and FP8 attention
+with its pre-pass and where it stands against the FP8 accuracy bar), and config.targets: the
+bf16 and FP8 fractions of peak against their goals.
 """
 from __future__ import annotations
 
@@ -85,36 +94,56 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mha16k", choices=["mha16k", "sweep", "causal", "varlen", "fp8", "fp8_causal",
                                                               "fp8_varlen", "window", "bwd"])
+    ap.add_argument("--config", default=None,
+                    help="with --workload sweep or causal: run only this configuration (e.g. mha_n512_b32_h16_d128), "
+                         "for profiling one kernel instance")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time of the headline baseline")
+    ap.add_argument("--oracle-seconds", type=float, default=1.0,
+                    help="target oracle time of each other workload's figure (default run)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="before timing, run one elementwise copy (negation) of this many MiB, so that "
                          "profiler byte counters can be scaled against a kernel of known traffic")
     return ap.parse_args()
 
 
-def cpu_baseline(inp, target_s: float) -> dict:
-    """Time the fp64 oracle on successive chunks of query rows until about target_s elapse."""
+def cpu_baseline(inp, target_s: float, threads: int | None = None) -> dict:
+    """Time the fp64 oracle on successive chunks of random (head, query) rows of the workload
+    until about target_s elapse (every visible key of each row); with ``threads``, on that many
+    OpenMP threads.  Returns attention-FLOP throughput (4 d FLOP per visible key)."""
     import oracle
 
     q, k, v = (oracle.widen(getattr(inp, n), inp.dtype) for n in "qkv")
     rng = np.random.default_rng(123)
-    T = inp.B * inp.N
+    cu = inp.cu_seqlens.astype(np.int64) if inp.cu_seqlens is not None else np.arange(inp.B + 1) * inp.N
+    T = int(cu[-1])
     rows = 0
     flops = 0.0
     chunk = 1024
-    t0 = time.perf_counter()
-    while True:
-        heads = rng.integers(0, inp.Hq, chunk)
-        tokens = rng.integers(0, T, chunk)
-        oracle.attention_rows(q, k, v, heads, tokens, causal=inp.causal, alpha=inp.alpha)
-        rows += chunk
-        keys = (tokens % inp.N + 1) if inp.causal else np.full(chunk, inp.N)
-        flops += float(np.sum(4.0 * keys * inp.d))
-        el = time.perf_counter() - t0
-        if el >= target_s or el >= 30.0:
-            break
-    return {"value": float(f"{flops / el / 1e12:.4g}"), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+    default_threads = oracle.num_threads()
+    if threads is not None:
+        oracle.set_num_threads(threads)
+    try:
+        t0 = time.perf_counter()
+        while True:
+            heads = rng.integers(0, inp.Hq, chunk)
+            tokens = rng.integers(0, T, chunk)
+            oracle.attention_rows(q, k, v, heads, tokens, causal=inp.causal, alpha=inp.alpha,
+                                  cu_seqlens=inp.cu_seqlens, window=inp.window)
+            rows += chunk
+            seq = np.searchsorted(cu, tokens, side="right") - 1
+            i = tokens - cu[seq]
+            keys = (i + 1) if inp.causal else (cu[seq + 1] - cu[seq])
+            if inp.window:
+                keys = np.minimum(keys, inp.window)
+            flops += float(np.sum(4.0 * keys * inp.d))
+            el = time.perf_counter() - t0
+            if el >= target_s or el >= 30.0:
+                break
+        used = oracle.num_threads()
+    finally:
+        oracle.set_num_threads(default_threads)
+    return {"value": float(f"{flops / el / 1e12:.4g}"), "unit": "TFLOP/s", "cores": used,
             "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{rows} random (head, query) rows of the same workload, all keys each, fp64, {el:.1f} s"}
 
@@ -165,6 +194,68 @@ def cpu_model() -> str:
     return "unknown"
 
 
+def sustained_clock(step, seconds: float = 2.5, settle: float = 1.2):
+    """The graphics clock and socket power while ``step`` runs back to back for ``seconds``.
+
+    Source: amdsmi gpu_metrics, current_gfxclk of each XCD (an average the power-management
+    firmware refreshes about once a second) and current socket power.  Readings taken in the
+    first ``settle`` seconds still cover time before the load began and are dropped.  These are
+    reads of the management interface only; nothing else is launched.  Returns None when the
+    interface is unavailable."""
+    import threading
+
+    import torch
+
+    try:
+        import amdsmi
+
+        amdsmi.amdsmi_init()
+        handles = amdsmi.amdsmi_get_processor_handles()
+        handle = handles[0] if len(handles) == 1 else None
+        if handle is None:
+            bus = getattr(torch.cuda.get_device_properties(torch.cuda.current_device()), "pci_bus_id", None)
+            for h in handles:
+                if bus is not None and int(amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")[1], 16) == int(bus):
+                    handle = h
+        if handle is None:
+            return None
+    except Exception:  # noqa: BLE001 -- no management interface: report no clock
+        return None
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                m = amdsmi.amdsmi_get_gpu_metrics_info(handle)
+            except Exception:  # noqa: BLE001
+                return
+            clks = m.get("current_gfxclks")
+            vals = [x for x in clks if isinstance(x, (int, float)) and 0 < x < 10000] if isinstance(clks, list) else []
+            pw = m.get("current_socket_power")
+            samples.append((time.perf_counter(), sum(vals) / len(vals) if vals else None,
+                            pw if isinstance(pw, (int, float)) and 0 < pw < 100000 else None))
+            stop.wait(0.05)
+
+    th = threading.Thread(target=poll, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    clk = [c for t, c, _ in samples if t - t0 >= settle and c is not None]
+    pw = [p for t, _, p in samples if t - t0 >= settle and p is not None]
+    if not clk:
+        return None
+    return {"mean_mhz": round(float(np.mean(clk)), 1), "min_mhz": round(float(np.min(clk)), 1),
+            "max_mhz": round(float(np.max(clk)), 1), "socket_power_w": round(float(np.mean(pw)), 1) if pw else None,
+            "samples": len(clk), "window_s": seconds - settle,
+            "source": "amdsmi gpu_metrics current_gfxclk (firmware average per XCD, refreshed about once a "
+                      "second), sampled while the same launch ran back to back after the timed region"}
+
+
 def to_dev(bits, dtype, dev):
     import torch
 
@@ -188,6 +279,12 @@ def line(args, name, inp, flops, ms_wall, ms_gpu, dtype, extra=None, traffic=Non
                     "tflops_launch_best": round(flops / (best * 1e-3) / 1e12, 2)})
     if extra:
         cfg.update(extra)
+    clk = cfg.get("sclk")
+    if clk:
+        # the nominal peak assumes 2.4 GHz; the same units at the observed mean clock
+        at_clk = peak * clk["mean_mhz"] / 2400.0
+        cfg["peak_at_observed_sclk"] = round(at_clk, 1)
+        cfg["pct_of_peak_at_observed_sclk"] = round(100 * achieved / at_clk, 2)
     return {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_wall, 4), "higher_is_better": True, "scaling": "weak",
@@ -198,7 +295,7 @@ def line(args, name, inp, flops, ms_wall, ms_gpu, dtype, extra=None, traffic=Non
     }
 
 
-def run_16bit(args, name, inp, dev, stream, traffic=None, cpu=False):
+def run_16bit(args, name, inp, dev, stream, traffic=None, cpu=False, oracle_s=0.0, clock=False):
     import torch
 
     import exact_attention_76_amd as ea
@@ -223,8 +320,11 @@ def run_16bit(args, name, inp, dev, stream, traffic=None, cpu=False):
     ms_wall, ms_gpu = timed(step, stream, args.steps, args.warmup)
     launches = per_launch(step, stream, args.steps)
     cpu_res = cpu_baseline(inp, args.cpu_seconds) if cpu and not args.no_cpu_baseline else None
+    extra = {"sclk": sustained_clock(step)} if clock else {}
+    if oracle_s > 0 and not args.no_cpu_baseline:
+        extra["oracle"] = cpu_baseline(inp, oracle_s)
     return line(args, name, inp, inp.flops(), ms_wall, ms_gpu, inp.dtype, traffic=traffic, cpu=cpu_res,
-                launches=launches)
+                launches=launches, extra=extra)
 
 
 # FP8 workloads: name of the line -> the seeded bf16 inputs it quantises
@@ -241,7 +341,7 @@ def window_inputs():
     return inp
 
 
-def run_fp8(args, dev, stream, workload="fp8", inp=None):
+def run_fp8(args, dev, stream, workload="fp8", inp=None, oracle_s=0.0, clock=False):
     import torch
 
     import exact_attention_76_amd as ea
@@ -271,6 +371,7 @@ def run_fp8(args, dev, stream, workload="fp8", inp=None):
 
     ms_wall, ms_gpu = timed(attn, stream, args.steps, args.warmup)
     launches = per_launch(attn, stream, args.steps)
+    clk = sustained_clock(attn) if clock else None
     pw, pg = timed(prep, stream, args.steps, args.warmup)
     elems = q.numel() + k.numel() + v.numel()
     prep_bytes = 2 * elems + elems + (qs.numel() + ks.numel() + vs.numel()) * 4 + inp.d
@@ -291,7 +392,7 @@ def run_fp8(args, dev, stream, workload="fp8", inp=None):
                                                 "frac": round(rbytes / (rg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                                 "bytes_per_launch": rbytes},
                       "rope_unfused_extra_bytes": 4 * (q.numel() + k.numel())}
-    extra = {"attention_only": True, "hadamard": True, "inputs_from": src,
+    extra = {"attention_only": True, "hadamard": True, "inputs_from": src, "sclk": clk,
              "prepare_ms": round(pw, 4),
              "prepare_roofline": {"bound": "hbm", "achieved": round(prep_bytes / (pg * 1e-3) / 1e9, 1),
                                   "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -299,11 +400,54 @@ def run_fp8(args, dev, stream, workload="fp8", inp=None):
                                   "traffic": measured_traffic("fp8_prepare") if workload == "fp8" else None,
                                   "bytes_per_launch": prep_bytes},
              "prepare_plus_attention_tflops": round(inp.flops() / ((pw + ms_wall) * 1e-3) / 1e12, 2), **rope_extra}
+    if workload == "fp8" and inp.window == 0:
+        extra["accuracy"] = fp8_accuracy_note()
+    if oracle_s > 0 and not args.no_cpu_baseline:
+        extra["oracle"] = cpu_baseline(inp, oracle_s)
     name = "fp8_b2_h16_n8192_d128" if workload == "fp8" else f"fp8_{src}"
     if inp.window:
         name = f"fp8_window{inp.window}_b1_h16_n16384_d128"
     return line(args, name, inp, inp.flops(), ms_wall, ms_gpu, "fp8", extra=extra,
                 traffic=measured_traffic("fp8_attention") if workload == "fp8" else None, launches=launches)
+
+
+def fp8_accuracy_note() -> dict:
+    """Where the FP8 workload stands against the FP8 bar (O RMSE <= 3e-2 against fp64 on the
+    unquantised inputs), from the floor the tests pin on the CPU from the oracle alone."""
+    floor = None
+    try:
+        for line_ in open(os.path.join(ROOT, "tests", "golden", "fp8_quantisation_floors.txt")):
+            if line_.startswith("c5_shared_channels "):
+                floor = float(line_.split()[1])
+    except OSError:
+        pass
+    return {"bar_rmse": 3e-2, "quantisation_floor_rmse": floor,
+            "reading": "two x20 outlier channels shared by Q, K and V: quantising the inputs alone "
+                       "(exact attention on the e4m3-dequantised inputs) already costs the floor, above "
+                       "the bar, so the bar is not met on this reading (the kernel measures about 0.036 "
+                       "and is held to the floor + 2e-3); with independent outlier channels per tensor the "
+                       "floor is 0.011 and the kernel meets the bar",
+            "floor_source": "tests/golden/fp8_quantisation_floors.txt (oracle only)"}
+
+
+def summary(r: dict) -> dict:
+    """The figures of one bench line that the headline line carries for it."""
+    c = r["config"]
+    out = {"tflops": r["value"], "pct_of_peak": c["pct_of_peak"], "dtype": r["dtype"],
+           "ms_per_step": r["ms_per_step"], "roofline_frac": r["roofline"]["frac"],
+           "tflops_launch_median": c.get("tflops_launch_median")}
+    for key in ("peak_at_observed_sclk", "pct_of_peak_at_observed_sclk"):
+        if key in c:
+            out[key] = c[key]
+    if c.get("sclk"):
+        out["sclk_mean_mhz"] = c["sclk"]["mean_mhz"]
+    if c.get("oracle"):
+        out["oracle_tflops"] = c["oracle"]["value"]
+        out["oracle_cores"] = c["oracle"]["cores"]
+    for key in ("prepare_ms", "prepare_roofline", "prepare_plus_attention_tflops", "accuracy"):
+        if key in c:
+            out[key] = c[key]
+    return out
 
 
 def run_bwd(args, name, inp, dev, stream):
@@ -353,29 +497,51 @@ def main():
         if args.workload == "mha16k":
             name = "mha_n16384_b1_h16_d128"
             head = run_16bit(args, name, si.CONFIGS[name](), dev, stream, traffic=measured_traffic("bf16_mha16k"),
-                             cpu=True)
+                             cpu=True, oracle_s=args.oracle_seconds, clock=True)
             # the rest of the B*N = 16384 sweep this figure belongs to, attached for context
             sweep, flops, ms = {}, 0.0, 0.0
+            workloads = {}
             for n in si.CONFIGS:
                 if not n.startswith("mha_n"):
                     continue
-                r = head if n == name else run_16bit(args, n, si.CONFIGS[n](), dev, stream)
+                r = head if n == name else run_16bit(args, n, si.CONFIGS[n](), dev, stream,
+                                                      oracle_s=args.oracle_seconds)
                 sweep[f"N={r['config']['N']}"] = r["value"]
+                workloads[n] = summary(r)
                 flops += r["config"]["flops_per_step"]
                 ms += r["ms_per_step"]
             head["config"]["sweep_tflops"] = sweep
             head["config"]["sweep_aggregate_tflops"] = round(flops / (ms * 1e-3) / 1e12, 2)
+            # every other workload, timed the same way: the smallest (launch-bound), the causal
+            # head dims, the packed causal GQA workload and FP8 (attention and pre-pass)
+            for n in ["mha_b1_h2_n128_d64"] + [c for c in si.CONFIGS if c.startswith("causal")] + \
+                     ["gqa_varlen_causal_hq32_hkv8_d128"]:
+                workloads[n] = summary(run_16bit(args, n, si.CONFIGS[n](), dev, stream, oracle_s=args.oracle_seconds))
+            r8 = run_fp8(args, dev, stream, "fp8", oracle_s=args.oracle_seconds, clock=True)
+            workloads["fp8_b2_h16_n8192_d128"] = summary(r8)
+            head["config"]["workloads"] = workloads
+            head["config"]["targets"] = {
+                "bf16_headline_pct_of_peak": {"target": 60.0, "measured": head["config"]["pct_of_peak"]},
+                "fp8_pct_of_peak": {"target": 45.0, "measured": workloads["fp8_b2_h16_n8192_d128"]["pct_of_peak"]}}
+            if head["cpu_baseline"] is not None:
+                cb = head["cpu_baseline"]
+                cb["per_config"] = {n: {"tflops": w["oracle_tflops"], "cores": w["oracle_cores"]}
+                                    for n, w in workloads.items() if "oracle_tflops" in w}
+                # the same oracle on one core, for a per-core figure
+                cb["one_core"] = {n: cpu_baseline(si.CONFIGS[n](), args.oracle_seconds * 2, threads=1)
+                                  for n in ("mha_b1_h2_n128_d64", "mha_n4096_b4_h16_d128")}
             out = [head]
         elif args.workload == "sweep":
-            out = [run_16bit(args, n, si.CONFIGS[n](), dev, stream)
-                   for n in si.CONFIGS if n.startswith("mha_n")]
+            out = [run_16bit(args, n, si.CONFIGS[n](), dev, stream, clock=True)
+                   for n in si.CONFIGS if n.startswith("mha_n") and args.config in (None, n)]
         elif args.workload == "causal":
-            out = [run_16bit(args, n, si.CONFIGS[n](), dev, stream) for n in si.CONFIGS if n.startswith("causal")]
+            out = [run_16bit(args, n, si.CONFIGS[n](), dev, stream, clock=True)
+                   for n in si.CONFIGS if n.startswith("causal") and args.config in (None, n)]
         elif args.workload == "varlen":
             n = "gqa_varlen_causal_hq32_hkv8_d128"
-            out = [run_16bit(args, n, si.CONFIGS[n](), dev, stream)]
+            out = [run_16bit(args, n, si.CONFIGS[n](), dev, stream, clock=True)]
         elif args.workload in FP8_WORKLOADS:
-            out = [run_fp8(args, dev, stream, args.workload)]
+            out = [run_fp8(args, dev, stream, args.workload, clock=True)]
         elif args.workload == "bwd":
             out = [run_bwd(args, "bwd_" + n, si.CONFIGS[n](), dev, stream)
                    for n in ("mha_n16384_b1_h16_d128", "causal_b2_h16_n8192_d128")]

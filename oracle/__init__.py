@@ -54,10 +54,15 @@ class OracleLib:
                                          ctypes.c_double, P, P]
         lib.oracle_attention.restype = ctypes.c_int
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_num_threads.restype = None
         self.lib = lib
 
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())
+
+    def set_num_threads(self, n: int) -> None:
+        self.lib.oracle_set_num_threads(int(n))
 
     def attention(self, q, k, v, *, causal: bool = False, alpha: float | None = None, cu_seqlens=None,
                   window: int = 0):
@@ -150,6 +155,11 @@ def _pack(q, k, v, cu_seqlens):
 
 def num_threads() -> int:
     return _load().num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads of the following oracle calls (the benchmark's one-core figure uses 1)."""
+    _load().set_num_threads(n)
 
 
 def attention(q, k, v, **kw):

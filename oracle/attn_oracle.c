@@ -123,6 +123,17 @@ int oracle_attention(const double* q, const double* k, const double* v,
   return 0;
 }
 
+/* Number of OpenMP threads the calls above use from now on (n >= 1); the benchmark's CPU
+ * baseline takes a one-core figure with n = 1. */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  extern void omp_set_num_threads(int);
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* Number of OpenMP threads the calls above use (reported next to oracle timings). */
 int oracle_num_threads(void) {
 #ifdef _OPENMP
