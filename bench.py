@@ -57,19 +57,19 @@ METRIC = "attention fwd TFLOPs/s (4·B·H·N²·d, ½ if causal) and % of MI355X
 PEAK = {"bf16": 2516.6, "fp8": 5033.2}  # dense MFMA TFLOP/s: 256 CU x (4096 | 8192) FLOP/clk x 2.4 GHz
 HBM_PEAK_GBS = 8000.0
 # HBM-side bytes per launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE, each scaled by what the
-# same counter reads for a copy kernel of known size (profiles/*_traffic.md).  An entry is valid
+# same counter reads for a copy kernel of known size (profiles/*_counters.md).  An entry is valid
 # only for the kernel sources it was taken on (sha256 prefix of each file); any other version
 # reports null.
 _DEC = "exact_attention_76_amd/csrc/decompose.h"
 _T16 = "exact_attention_76_amd/csrc/tile16.h"
 MEASURED_TRAFFIC = {
-    "bf16_mha16k": {"sources": {"exact_attention_76_amd/csrc/attn_fwd.hip": "ee3128d159a6e036",
-                                _DEC: "5177b80538cd69cc", _T16: "91339639cbec1225"},
-                    "bytes": 403999164},
-    "fp8_attention": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "11506b4cbf68a36c",
-                                  _DEC: "5177b80538cd69cc"}, "bytes": 185916504},
-    "fp8_prepare": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "11506b4cbf68a36c"},
-                    "bytes": 302622270},
+    "bf16_mha16k": {"sources": {"exact_attention_76_amd/csrc/attn_fwd.hip": "0faf659f260de746",
+                                _DEC: "2521a203b68b3442", _T16: "91339639cbec1225"},
+                    "bytes": 403985174},
+    "fp8_attention": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "7b57f8130a1f7ca0",
+                                  _DEC: "2521a203b68b3442"}, "bytes": 185855853},
+    "fp8_prepare": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "7b57f8130a1f7ca0"},
+                    "bytes": 302604536},
 }
 
 
@@ -98,6 +98,8 @@ def parse():
                     help="with --workload sweep or causal: run only this configuration (e.g. mha_n512_b32_h16_d128), "
                          "for profiling one kernel instance")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the sustained-load clock reading (2.5 s of extra launches), e.g. under a profiler")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time of the headline baseline")
     ap.add_argument("--oracle-seconds", type=float, default=1.0,
                     help="target oracle time of each other workload's figure (default run)")
@@ -320,7 +322,7 @@ def run_16bit(args, name, inp, dev, stream, traffic=None, cpu=False, oracle_s=0.
     ms_wall, ms_gpu = timed(step, stream, args.steps, args.warmup)
     launches = per_launch(step, stream, args.steps)
     cpu_res = cpu_baseline(inp, args.cpu_seconds) if cpu and not args.no_cpu_baseline else None
-    extra = {"sclk": sustained_clock(step)} if clock else {}
+    extra = {"sclk": sustained_clock(step)} if clock and not args.no_clock else {}
     if oracle_s > 0 and not args.no_cpu_baseline:
         extra["oracle"] = cpu_baseline(inp, oracle_s)
     return line(args, name, inp, inp.flops(), ms_wall, ms_gpu, inp.dtype, traffic=traffic, cpu=cpu_res,
@@ -371,7 +373,7 @@ def run_fp8(args, dev, stream, workload="fp8", inp=None, oracle_s=0.0, clock=Fal
 
     ms_wall, ms_gpu = timed(attn, stream, args.steps, args.warmup)
     launches = per_launch(attn, stream, args.steps)
-    clk = sustained_clock(attn) if clock else None
+    clk = sustained_clock(attn) if clock and not args.no_clock else None
     pw, pg = timed(prep, stream, args.steps, args.warmup)
     elems = q.numel() + k.numel() + v.numel()
     prep_bytes = 2 * elems + elems + (qs.numel() + ks.numel() + vs.numel()) * 4 + inp.d
