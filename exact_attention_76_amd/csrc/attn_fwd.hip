@@ -19,7 +19,8 @@
 //     operand layout: permuting P's columns together with V's rows leaves P V unchanged.)
 //   * K and V tiles are copied buffer-to-LDS (no registers, no VALU) while earlier tiles are
 //     multiplied.  Two loops: the plain one (two K and two V buffers, one barrier per tile,
-//     the two waves of a SIMD overlapping freely) and, for d = 128 and 256, a ping-pong loop
+//     the two waves of a SIMD overlapping freely) and, for d = 256 and d = 128 (short non-causal
+//     sequences aside), a ping-pong loop
 //     (the digest's section 3.3 idea, enforced with workgroup barriers): the two halves of the
 //     workgroup run one phase apart, so that on every SIMD one wave multiplies while the other
 //     takes its softmax; operand reads run a few products ahead of the matrix instructions,
@@ -481,6 +482,12 @@ hipError_t launch_modes(const FwdArgs& a, hipStream_t stream) {
 }
 
 template <int D, int BC, typename SH, bool BF16>
+hipError_t launch_noncausal(const FwdArgs& a, hipStream_t stream) {
+  return a.cu_seqlens != nullptr ? launch<D, BC, SH, BF16, false, true>(a, stream)
+                                 : launch<D, BC, SH, BF16, false, false>(a, stream);
+}
+
+template <int D, int BC, typename SH, bool BF16>
 hipError_t launch_window(const FwdArgs& a, hipStream_t stream) {
   return a.cu_seqlens != nullptr ? launch<D, BC, SH, BF16, true, true, true>(a, stream)
                                  : launch<D, BC, SH, BF16, true, false, true>(a, stream);
@@ -491,7 +498,16 @@ hipError_t launch_window(const FwdArgs& a, hipStream_t stream) {
 // the ping-pong loop (measured on MI355X: +4-7% over the plain loop); at d = 64 the softmax
 // outweighs the products and the plain loop, which lets the two waves of a SIMD share the
 // VALU freely, is as fast.  With a sliding window, d = 256 runs the plain loop: the window's
-// bookkeeping does not fit the ping-pong loop's 256 registers without spilling.
+// bookkeeping does not fit the ping-pong loop's 256 registers without spilling.  Non-causal
+// d = 128 with at most kShortKeys keys per sequence (eight tiles) runs the plain loop too: a
+// workgroup then lives for only a few tiles, and the ping-pong loop's extra phase at either
+// end (the second half starts one phase late and finishes one phase after the first) costs
+// more than its overlap gains (measured: +5-8% at N = 512, even at N = 1024, and the ping-pong
+// loop ahead from N = 2048 on).
+constexpr int kShortKeys = 512;
+#ifndef ATTN_D128_SHORT_SHAPE
+#define ATTN_D128_SHORT_SHAPE 64, LoopShape<8>
+#endif
 #ifndef ATTN_D64_SHAPE
 #define ATTN_D64_SHAPE 64, LoopShape<8>
 #endif
@@ -517,7 +533,9 @@ hipError_t launch_dims(const FwdArgs& a, hipStream_t stream) {
   }
   switch (a.d) {
     case 64: return launch_modes<64, ATTN_D64_SHAPE, BF16>(a, stream);
-    case 128: return launch_modes<128, ATTN_D128_SHAPE, BF16>(a, stream);
+    case 128:
+      if (!a.causal && a.N <= kShortKeys) return launch_noncausal<128, ATTN_D128_SHORT_SHAPE, BF16>(a, stream);
+      return launch_modes<128, ATTN_D128_SHAPE, BF16>(a, stream);
     case 256: return launch_modes<256, ATTN_D256_SHAPE, BF16>(a, stream);
     default: return hipErrorInvalidValue;
   }

@@ -50,10 +50,10 @@ def test_fp8_variant_on_outlier_mixture(rotate, per_tensor):
     o, lse = o.double().cpu().numpy(), lse.double().cpu().numpy()
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     heads, tokens = gu.sample_rows(inp, ROWS, seed=3)
-    X, Y, Z, lse_dq = _three_errors(inp, o, lse, prep, heads, tokens)
+    X, Y, Z, own = _three_errors(inp, o, lse, prep, heads, tokens, rotated=rotate)
     gu.say(f"ABLATION fp8 rotate={rotate} per_tensor={per_tensor}: O RMSE vs fp64 {X['rmse']:.3e} "
            f"(input-quantisation floor {Y['rmse']:.3e}, kernel vs dequantised {Z['rmse']:.3e})")
-    check_fp8(X, Y, Z, lse_dq)
+    check_fp8(X, Y, Z, own)
 
 
 # Significant bits of the 16-bit formats: rounding to them costs a relative error of at most 2^-p.

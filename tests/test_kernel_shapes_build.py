@@ -19,7 +19,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # source file -> (kernel name fragment, number of instances the dispatch builds)
 KERNELS = {
-    "attn_fwd.hip": ("fwd_kernel", 2 * 3 * 6),  # bf16/fp16 x d 64/128/256 x 4 modes + 2 windowed
+    # bf16/fp16 x (d 64/128/256 x (4 modes + 2 windowed) + the short non-causal d = 128 shape x 2 modes)
+    "attn_fwd.hip": ("fwd_kernel", 2 * (3 * 6 + 2)),
     "fp8.hip": ("fwd_fp8_kernel", 6),            # 4 modes + 2 windowed
     "attn_bwd.hip": ("bwd_", None),
 }

@@ -1,7 +1,7 @@
 """GPU parity of attn_fwd (16-bit inputs) against the fp64 oracle on the same seeded inputs.
 
-* small problems that span several 128-query and 64-key tiles with ragged tails: every element
-  of O and LSE is compared;
+* small problems that span several 256-query and 64-key tiles with ragged tails, on both
+  sides of every loop-shape switch: every element of O and LSE is compared;
 * closed forms the kernel must reproduce: a causal first row is a bit-exact copy of V_0;
   Q = 0 gives the mean of the visible V rows and L = ln(count);
 * the five workloads at full size, in the benchmark's launch configuration: O and LSE start as
@@ -44,6 +44,21 @@ def test_smallest_workload_every_element():
 def test_ragged_multi_tile(d, causal, dtype):
     inp = si.dense_inputs(2, 300, 4, d, Hkv=2, causal=causal, seed=100 + d + 7 * causal, dtype=dtype)
     _compare_full(inp, f"ragged d={d} causal={causal} {dtype}")
+
+
+# Non-causal d = 128 takes the plain tile loop up to 512 keys per sequence and the ping-pong
+# loop above that: both sides of the switch, with ragged query blocks and key tiles.
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("N", [512, 513, 700])
+def test_noncausal_d128_both_loops(N, dtype):
+    inp = si.dense_inputs(2, N, 4, 128, Hkv=2, causal=False, seed=900 + N, dtype=dtype)
+    _compare_full(inp, f"non-causal d=128 N={N} {dtype}")
+
+
+@pytest.mark.parametrize("lengths", [[300, 512, 5], [700, 33, 513, 1]])
+def test_varlen_noncausal_d128_both_loops(lengths):
+    inp = si.varlen_inputs(lengths, 4, 2, 128, causal=False, seed=910 + len(lengths))
+    _compare_full(inp, f"varlen non-causal d=128 lengths={lengths}")
 
 
 @pytest.mark.parametrize("causal", [False, True])
