@@ -1,7 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of the fused attention forward pass on one MI355X.
 
-One step = one attn_fwd call over the whole workload, inputs already resident in HBM.
+One step = one attn_fwd call over the whole workload, inputs already resident in HBM.  Each
+workload runs at least --warmup untimed steps, and keeps warming up until --warmup-seconds
+(0.2 s) have passed, so that the timed steps run at the clock the chip settles at under load.
 Default workload (the headline line): non-causal multi-head attention, bf16, B=1, N=16384,
 H=16, d=128 -- the longest point of the B*N = 16384-token sweep (the pages quote their d=128
 non-causal figure at 16k); the line's config also carries every point of that sweep and the
@@ -92,6 +94,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup-seconds", type=float, default=0.2,
+                    help="keep warming up (in rounds of --warmup steps) until this much time has passed; "
+                         "0 gives exactly --warmup steps, e.g. for a fixed dispatch count under a profiler")
     ap.add_argument("--workload", default="mha16k", choices=["mha16k", "sweep", "causal", "varlen", "fp8", "fp8_causal",
                                                               "fp8_varlen", "window", "bwd"])
     ap.add_argument("--config", default=None,
@@ -150,15 +155,22 @@ def cpu_baseline(inp, target_s: float, threads: int | None = None) -> dict:
             "sample": f"{rows} random (head, query) rows of the same workload, all keys each, fp64, {el:.1f} s"}
 
 
-def timed(step, stream, steps, warmup):
-    """W untimed steps, then K steps between two synchronisations.  Returns (wall ms per step,
-    event ms per step measured on ``stream``)."""
+def timed(step, stream, steps, warmup, min_seconds=0.0):
+    """At least W untimed steps, continued until ``min_seconds`` of them have run (the clock
+    needs that long under load to settle; a short step's 20 warmups take a few ms), then K
+    steps between two synchronisations.  Returns (wall ms per step, event ms per step measured
+    on ``stream``)."""
     import torch
 
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    while time.perf_counter() - t0 < min_seconds:
+        for _ in range(max(1, warmup)):
+            step()
+        torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record(stream)
@@ -271,7 +283,8 @@ def line(args, name, inp, flops, ms_wall, ms_gpu, dtype, extra=None, traffic=Non
     achieved = flops / (ms_gpu * 1e-3) / 1e12
     cfg = {"workload": name, "B": inp.B, "N": inp.N, "Hq": inp.Hq, "Hkv": inp.Hkv, "d": inp.d,
            "causal": inp.causal, "varlen": inp.cu_seqlens is not None, "tokens": inp.total_tokens,
-           "flops_per_step": flops, "pct_of_peak": round(100 * tflops / peak, 2), "parallelism": "single GPU"}
+           "flops_per_step": flops, "pct_of_peak": round(100 * tflops / peak, 2), "parallelism": "single GPU",
+           "warmup_min_seconds": args.warmup_seconds}
     if inp.window:
         cfg["window"] = inp.window
     if launches is not None:
@@ -319,7 +332,7 @@ def run_16bit(args, name, inp, dev, stream, traffic=None, cpu=False, oracle_s=0.
             ea.attn_fwd(q, k, v, o, lse, causal=inp.causal, alpha=inp.alpha, cu_seqlens=cu,
                         max_seqlen=inp.N if cu is not None else None, stream=stream)
 
-    ms_wall, ms_gpu = timed(step, stream, args.steps, args.warmup)
+    ms_wall, ms_gpu = timed(step, stream, args.steps, args.warmup, args.warmup_seconds)
     launches = per_launch(step, stream, args.steps)
     cpu_res = cpu_baseline(inp, args.cpu_seconds) if cpu and not args.no_cpu_baseline else None
     extra = {"sclk": sustained_clock(step)} if clock and not args.no_clock else {}
@@ -371,10 +384,10 @@ def run_fp8(args, dev, stream, workload="fp8", inp=None, oracle_s=0.0, clock=Fal
     def prep():
         ea.attn_fp8_prepare_ex(q, k, v, q8, k8, v8, qs, ks, vs, hadamard_signs=signs, stream=stream, **packed)
 
-    ms_wall, ms_gpu = timed(attn, stream, args.steps, args.warmup)
+    ms_wall, ms_gpu = timed(attn, stream, args.steps, args.warmup, args.warmup_seconds)
     launches = per_launch(attn, stream, args.steps)
     clk = sustained_clock(attn) if clock and not args.no_clock else None
-    pw, pg = timed(prep, stream, args.steps, args.warmup)
+    pw, pg = timed(prep, stream, args.steps, args.warmup, args.warmup_seconds)
     elems = q.numel() + k.numel() + v.numel()
     prep_bytes = 2 * elems + elems + (qs.numel() + ks.numel() + vs.numel()) * 4 + inp.d
     rope_extra = {}
@@ -386,7 +399,7 @@ def run_fp8(args, dev, stream, workload="fp8", inp=None, oracle_s=0.0, clock=Fal
             ea.attn_fp8_prepare_ex(q, k, v, q8, k8, v8, qs, ks, vs, hadamard_signs=signs, rope_cos=cos, rope_sin=sin,
                                    stream=stream)
 
-        rw, rg = timed(rope_prep, stream, args.steps, args.warmup)
+        rw, rg = timed(rope_prep, stream, args.steps, args.warmup, args.warmup_seconds)
         rbytes = prep_bytes + 2 * cos.numel() * 4
         rope_extra = {"rope_prepare_ms": round(rw, 4),
                       "rope_prepare_roofline": {"bound": "hbm", "achieved": round(rbytes / (rg * 1e-3) / 1e9, 1),
@@ -468,7 +481,7 @@ def run_bwd(args, name, inp, dev, stream):
     def step():
         ea.attn_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, causal=inp.causal, alpha=inp.alpha, stream=stream)
 
-    ms_wall, ms_gpu = timed(step, stream, args.steps, args.warmup)
+    ms_wall, ms_gpu = timed(step, stream, args.steps, args.warmup, args.warmup_seconds)
     launches = per_launch(step, stream, args.steps)
     return line(args, name, inp, 2.5 * inp.flops(), ms_wall, ms_gpu, inp.dtype, launches=launches,
                 extra={"pass": "backward", "flops_rule": "2.5 x forward (five products)"})
