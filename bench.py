@@ -67,11 +67,11 @@ _T16 = "exact_attention_76_amd/csrc/tile16.h"
 MEASURED_TRAFFIC = {
     "bf16_mha16k": {"sources": {"exact_attention_76_amd/csrc/attn_fwd.hip": "865bff5493eefff4",
                                 _DEC: "2521a203b68b3442", _T16: "91339639cbec1225"},
-                    "bytes": 404021813},
+                    "bytes": 404039867},
     "fp8_attention": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "7b57f8130a1f7ca0",
-                                  _DEC: "2521a203b68b3442"}, "bytes": 185855853},
+                                  _DEC: "2521a203b68b3442"}, "bytes": 185918981},
     "fp8_prepare": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "7b57f8130a1f7ca0"},
-                    "bytes": 302604536},
+                    "bytes": 302628740},
 }
 
 
