@@ -61,6 +61,28 @@ def test_varlen_noncausal_d128_both_loops(lengths):
     _compare_full(inp, f"varlen non-causal d=128 lengths={lengths}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_plain_and_ping_pong_loops_bit_identical(dtype):
+    """Both tile loops take the same tiles in the same key order with the same arithmetic, so
+    they must agree bit for bit.  The same packed non-causal d = 128 inputs run the plain loop
+    with max_seqlen = 512 and the ping-pong loop with max_seqlen = 1000 (a larger bound only
+    grows the grid; the extra blocks exit)."""
+    import torch
+
+    inp = si.varlen_inputs([300, 5, 512, 129], 4, 2, 128, causal=False, seed=920, dtype=dtype)
+    gu.say("plain vs ping-pong loop", dtype)
+    q, k, v, cu = gu.to_device(inp)
+    outs = []
+    for max_seqlen in (512, 1000):
+        o, lse = gu.attention_nan(q, k, v, causal=False, alpha=inp.alpha, cu_seqlens=cu, max_seqlen=max_seqlen)
+        torch.cuda.synchronize()
+        outs.append((o.float().cpu().numpy(), lse.cpu().numpy()))
+    (o1, l1), (o2, l2) = outs
+    assert np.all(np.isfinite(o1)) and np.all(np.isfinite(l1))
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    _compare_full(inp, f"plain loop, packed non-causal {dtype}")
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("d", [64, 128])
 def test_varlen_small(d, causal):
