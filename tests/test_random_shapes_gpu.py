@@ -36,9 +36,9 @@ def _draw(case: int):
         N = int(rng.integers(1, 1000))
         inp = si.dense_inputs(B, N, Hq, d, Hkv=Hkv, causal=mode != "none", seed=seed, dtype=dtype)
     else:
-        lengths = [int(x) for x in rng.integers(0, 800, int(rng.integers(1, 6)))]
-        if sum(lengths) == 0:
-            lengths[0] = 1
+        lengths = [int(x) for x in rng.integers(1, 800, int(rng.integers(1, 6)))]
+        if rng.random() < 1 / 3:  # an empty sequence somewhere in the pack
+            lengths.insert(int(rng.integers(0, len(lengths) + 1)), 0)
         inp = si.varlen_inputs(lengths, Hq, Hkv, d, causal=mode != "none", seed=seed, dtype=dtype)
     if mode == "window":
         inp.window = int(rng.integers(1, max(2, inp.N + 50)))
@@ -112,6 +112,8 @@ def test_draws_cover_the_modes():
     assert {k[1] for k in seen} == {64, 128, 256}
     assert {k[2] for k in seen} == {"none", "causal", "window"}
     assert {k[3] for k in seen} == {False, True}
+    assert any(inp.cu_seqlens is not None and np.any(np.diff(inp.cu_seqlens) == 0)
+               for inp, _ in map(_draw, range(N_CASES))), "no packed draw with an empty sequence"
     seen = set()
     for c in range(N_BWD):
         inp, _ = _draw_bwd(c)
