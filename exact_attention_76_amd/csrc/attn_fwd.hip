@@ -50,11 +50,18 @@ namespace {
 //             which takes a tile's exponentials one k-step at a time next to that k-step's
 //             products.
 //   PD        (ping-pong only) how many products ahead the LDS operand reads are issued.
-template <int WAVES_, bool PP_ = false, int PD_ = 4>
+//   PERSIST   (plain loop, non-causal dense inputs) a workgroup takes the query blocks
+//             blockIdx.x, blockIdx.x + G, ... (G workgroups, one per CU) in turn, as one stream
+//             of key tiles: the next block's first K/V tile is copied while the current block's
+//             last tile is multiplied, and its Q fragment loaded during the current block's first
+//             tile, so no block pays its start-up alone.  Every block must have an even number of
+//             key tiles (the two buffers then alternate the same way in every block).
+template <int WAVES_, bool PP_ = false, int PD_ = 4, bool PERSIST_ = false>
 struct LoopShape {
   static constexpr int WAVES = WAVES_;
   static constexpr bool PP = PP_;
   static constexpr int PD = PD_;
+  static constexpr bool PERSIST = PERSIST_;
 };
 
 // Workgroup barrier between ping-pong phases.  The asm statement is a compiler memory barrier
@@ -62,11 +69,12 @@ struct LoopShape {
 __device__ __forceinline__ void phase_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // WINDOW (implies CAUSAL): causal sliding window of `window` keys; otherwise `window` is unused.
+// `blocks`: the number of (sequence, head, query block) work items (used by PERSIST only).
 template <int D, int BC, typename SH, bool BF16, bool CAUSAL, bool VARLEN, bool WINDOW>
 __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     uint16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int N,
-    const int* __restrict__ cu_seqlens, int nseq, float alpha, int num_qblocks, int window) {
+    const int* __restrict__ cu_seqlens, int nseq, float alpha, int num_qblocks, int window, int blocks) {
   constexpr int WAVES = SH::WAVES;
   constexpr int BR = 32 * WAVES;                   // queries per workgroup
   constexpr int NCH = D / 8;                       // 16-byte chunks per row
@@ -107,22 +115,25 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
     seq_start = b * N;
     n = N;
   }
-  const int q0 = qb * BR;
+  int q0 = qb * BR;
   if (q0 >= n) return;  // whole workgroup: block lies past the end of this sequence
-  const int g = h / (Hq / Hkv);
+  int g = h / (Hq / Hkv);
   const int64_t qstride = (int64_t)Hq * D;
   const int rowbytes = Hkv * D * 2;  // distance between consecutive tokens of one K/V head
 
   // ---- Q fragment of this lane: query qi, d = 16*st + 8*hi .. +7 ----
-  const int qw = q0 + wave * 32;  // first query of this wave
-  const int qi = qw + l32;        // this lane's query (within the sequence)
-  u32x4 qf[KS_D];
-  {
-    const int row = qi < n ? qi : n - 1;
-    const uint16_t* qp = q + (int64_t)(seq_start + row) * qstride + (int64_t)h * D + 8 * hi;
+  int qw = q0 + wave * 32;  // first query of this wave
+  int qi = qw + l32;        // this lane's query (within the sequence)
+  // Q fragment of the block (seq_start_, h_, q0_) into dst
+  auto load_q = [&](int seq_start_, int h_, int q0_, u32x4* dst) {
+    const int qi_ = q0_ + wave * 32 + l32;
+    const int row = qi_ < n ? qi_ : n - 1;
+    const uint16_t* qp = q + (int64_t)(seq_start_ + row) * qstride + (int64_t)h_ * D + 8 * hi;
 #pragma unroll
-    for (int s = 0; s < KS_D; ++s) qf[s] = *reinterpret_cast<const u32x4*>(qp + 16 * s);
-  }
+    for (int s = 0; s < KS_D; ++s) dst[s] = *reinterpret_cast<const u32x4*>(qp + 16 * s);
+  };
+  u32x4 qf[KS_D];
+  load_q(seq_start, h, q0, qf);
 
   // ---- K/V copies ----
   int voff;
@@ -132,15 +143,18 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
     voff = row * rowbytes + chunk * 16;
   }
   const int blk_bytes = 16 * rowbytes;
-  const char* kbase = reinterpret_cast<const char*>(k) + ((int64_t)seq_start * Hkv + g) * D * 2;
-  const char* vbase = reinterpret_cast<const char*>(v) + ((int64_t)seq_start * Hkv + g) * D * 2;
+  // byte offset of the K (and V) rows of KV head g_ of the sequence starting at token seq_start_
+  auto kv_head = [&](int seq_start_, int g_) { return ((int64_t)seq_start_ * Hkv + g_) * D * 2; };
+  const char* kbase = reinterpret_cast<const char*>(k) + kv_head(seq_start, g);
+  const char* vbase = reinterpret_cast<const char*>(v) + kv_head(seq_start, g);
   const int nbytes = (n - 1) * rowbytes + D * 2;  // bytes of this head's K (or V) rows
   // rows at or past n fall outside the buffer and read as zero
-  auto issue_tile = [&](char* kdst, char* vdst, int tile) {
+  auto issue_tile_from = [&](const char* kb, const char* vb, char* kdst, char* vdst, int tile) {
     const int off = tile * BC * rowbytes;
-    copy_rows_to_lds<NI, IPB>(kbase + off, nbytes - off, kdst + wave * NI * 1024, voff, blk_bytes);
-    copy_rows_to_lds<NI, IPB>(vbase + off, nbytes - off, vdst + wave * NI * 1024, voff, blk_bytes);
+    copy_rows_to_lds<NI, IPB>(kb + off, nbytes - off, kdst + wave * NI * 1024, voff, blk_bytes);
+    copy_rows_to_lds<NI, IPB>(vb + off, nbytes - off, vdst + wave * NI * 1024, voff, blk_bytes);
   };
+  auto issue_tile = [&](char* kdst, char* vdst, int tile) { issue_tile_from(kbase, vbase, kdst, vdst, tile); };
 
   // ---- operand read offsets (bytes inside a tile), lane part ----
   // K (A operand of S^T = K Q^T): row 32*cb + l32, chunk 2*st + hi; the XOR term depends on st&1
@@ -269,7 +283,83 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
     l += rs0 + rs1;
   };
 
-  if constexpr (!SH::PP) {
+  // ---- epilogue of the current block: O / l, L = alpha*m + ln l ----
+  auto finish = [&]() {
+    const float lt = halves_sum(l);
+    if (qi < n) {
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      uint16_t* op = o + (int64_t)(seq_start + qi) * qstride + (int64_t)h * D + 4 * hi;
+#pragma unroll
+      for (int db = 0; db < NB_D; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          u32x2 pr = {pack2<BF16>(oacc[db][4 * gq + 0] * inv, oacc[db][4 * gq + 1] * inv),
+                      pack2<BF16>(oacc[db][4 * gq + 2] * inv, oacc[db][4 * gq + 3] * inv)};
+          *reinterpret_cast<u32x2*>(op + db * 32 + gq * 8) = pr;
+        }
+      if (hi == 0) {
+        const float L = lt > 0.f ? m * alpha + __logf(lt) : -INFINITY;
+        int64_t idx;
+        if constexpr (VARLEN) idx = (int64_t)h * cu_seqlens[nseq] + seq_start + qi;
+        else idx = ((int64_t)b * Hq + h) * N + qi;
+        lse[idx] = L;
+      }
+    }
+  };
+
+  if constexpr (SH::PERSIST) {
+    // ---- persistent stream of blocks: this workgroup's blocks blockIdx.x + i * G ----
+    // G is a multiple of 8 whenever a workgroup takes more than one block, so all of them belong
+    // to its XCD's share of the decomposition.  Each block has ntiles (even) tiles: tile j of a
+    // block sits in buffer j % 2, and the next block's tile 0 is copied into buffer 0 while the
+    // current block's last tile (buffer 1) is multiplied.
+    static_assert(!SH::PP && !CAUSAL && !VARLEN && !WINDOW, "persistent blocks: plain loop, non-causal, dense");
+    const int G = gridDim.x;
+    const int mine = (blocks - (int)blockIdx.x + G - 1) / G;
+    u32x4 qn[KS_D];
+    issue_tile(kb0, vb0, 0);
+    __builtin_amdgcn_s_waitcnt(0);  // Q fragments and the first tile have arrived
+    __syncthreads();
+    for (int i = 0;; ++i) {
+      const bool more = i + 1 < mine;
+      int nqb = 0, nh = 0, nb = 0;
+      if (more) decompose<false>((int)blockIdx.x + (i + 1) * G, num_qblocks, Hq, Hkv, nseq, nqb, nh, nb);
+      const int ng = nh / (Hq / Hkv);
+      const char* nkbase = reinterpret_cast<const char*>(k) + kv_head(nb * N, ng);
+      const char* nvbase = reinterpret_cast<const char*>(v) + kv_head(nb * N, ng);
+      for (int j = 0; j < ntiles; j += 2) {
+        issue_tile(kb1, vb1, j + 1);
+        if (j == 0 && more) load_q(nb * N, nh, nqb * BR, qn);  // held through this block
+        compute_tile(kb0, vb0, j);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (j + 2 < ntiles) issue_tile(kb0, vb0, j + 2);
+        else if (more) issue_tile_from(nkbase, nvbase, kb0, vb0, 0);
+        compute_tile(kb1, vb1, j + 1);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+      finish();
+      if (!more) return;
+      // the next block becomes the current one, with a fresh online softmax
+#pragma unroll
+      for (int db = 0; db < NB_D; ++db) oacc[db] = f32x16{};
+      m = -INFINITY;
+      l = 0.f;
+      thr = -INFINITY;
+      mc_cur = 0.f;
+#pragma unroll
+      for (int s = 0; s < KS_D; ++s) qf[s] = qn[s];
+      h = nh;
+      b = nb;
+      seq_start = nb * N;
+      q0 = nqb * BR;
+      qw = q0 + wave * 32;
+      qi = qw + l32;
+      kbase = nkbase;
+      vbase = nvbase;
+    }
+  } else if constexpr (!SH::PP) {
     // ---- main loop: two buffer pairs, unrolled by two so each half names its buffers ----
     issue_tile(kb0, vb0, t0);
     __builtin_amdgcn_s_waitcnt(0);  // Q fragments and the first tile have arrived
@@ -434,27 +524,7 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
     // barrier after its epilogue (below)
   }
 
-  // ---- epilogue: O / l, L = alpha*m + ln l ----
-  const float lt = halves_sum(l);
-  if (qi < n) {
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    uint16_t* op = o + (int64_t)(seq_start + qi) * qstride + (int64_t)h * D + 4 * hi;
-#pragma unroll
-    for (int db = 0; db < NB_D; ++db)
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        u32x2 pr = {pack2<BF16>(oacc[db][4 * gq + 0] * inv, oacc[db][4 * gq + 1] * inv),
-                    pack2<BF16>(oacc[db][4 * gq + 2] * inv, oacc[db][4 * gq + 3] * inv)};
-        *reinterpret_cast<u32x2*>(op + db * 32 + gq * 8) = pr;
-      }
-    if (hi == 0) {
-      const float L = lt > 0.f ? m * alpha + __logf(lt) : -INFINITY;
-      int64_t idx;
-      if constexpr (VARLEN) idx = (int64_t)h * cu_seqlens[nseq] + seq_start + qi;
-      else idx = ((int64_t)b * Hq + h) * N + qi;
-      lse[idx] = L;
-    }
-  }
+  finish();
   if constexpr (SH::PP) {
     if (wave < WAVES / 2) phase_barrier();
   }
@@ -469,7 +539,31 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((fwd_kernel<D, BC, SH, BF16, CAUSAL, VARLEN, WINDOW>), dim3((unsigned)grid), dim3(64 * SH::WAVES), 0,
                      stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                      static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, a.Hq, a.Hkv,
-                     a.N, a.cu_seqlens, a.B, a.alpha, nqb, a.window);
+                     a.N, a.cu_seqlens, a.B, a.alpha, nqb, a.window, (int)grid);
+  return hipGetLastError();
+}
+
+// Persistent blocks (LoopShape PERSIST, non-causal dense inputs): one workgroup per CU, at most
+// as many as there are blocks; when there are more blocks than CUs, the grid is the CU count
+// rounded down to a multiple of the 8 XCDs.
+template <int D, int BC, typename SH, bool BF16>
+hipError_t launch_persistent(const FwdArgs& a, hipStream_t stream) {
+  static_assert(SH::PERSIST, "persistent loop shape");
+  constexpr int BR = 32 * SH::WAVES;
+  const int nqb = (a.N + BR - 1) / BR;
+  const long long blocks = (long long)nqb * a.Hq * a.B;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  int dev = 0, cus = 0;
+  hipError_t err = stream != nullptr ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess) return err;
+  const long long slots = cus >= 8 ? cus / 8 * 8 : 1;
+  const long long grid = blocks < slots ? blocks : slots;
+  hipLaunchKernelGGL((fwd_kernel<D, BC, SH, BF16, false, false, false>), dim3((unsigned)grid), dim3(64 * SH::WAVES), 0,
+                     stream, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                     static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.o), a.lse, a.Hq, a.Hkv,
+                     a.N, nullptr, a.B, a.alpha, nqb, 0, (int)blocks);
   return hipGetLastError();
 }
 
@@ -503,10 +597,17 @@ hipError_t launch_window(const FwdArgs& a, hipStream_t stream) {
 // workgroup then lives for only a few tiles, and the ping-pong loop's extra phase at either
 // end (the second half starts one phase late and finishes one phase after the first) costs
 // more than its overlap gains (measured: +5-8% at N = 512, even at N = 1024, and the ping-pong
-// loop ahead from N = 2048 on).
+// loop ahead from N = 2048 on).  Dense non-causal d = 128 with at most kPersistKeys keys and an
+// even number of key tiles runs the plain loop over persistent blocks, which also hides each
+// block's start-up behind its predecessor (measured: +5% at N = 512 and +4% at N = 1024 over
+// the next best loop; 1% and 4% behind the ping-pong loop at N = 2048 and 4096).
 constexpr int kShortKeys = 512;
+constexpr int kPersistKeys = 1024;
 #ifndef ATTN_D128_SHORT_SHAPE
 #define ATTN_D128_SHORT_SHAPE 64, LoopShape<8>
+#endif
+#ifndef ATTN_D128_PERSIST_SHAPE
+#define ATTN_D128_PERSIST_SHAPE 64, LoopShape<8, false, 4, true>
 #endif
 #ifndef ATTN_D64_SHAPE
 #define ATTN_D64_SHAPE 64, LoopShape<8>
@@ -534,6 +635,8 @@ hipError_t launch_dims(const FwdArgs& a, hipStream_t stream) {
   switch (a.d) {
     case 64: return launch_modes<64, ATTN_D64_SHAPE, BF16>(a, stream);
     case 128:
+      if (!a.causal && a.cu_seqlens == nullptr && a.N <= kPersistKeys && ((a.N + 63) / 64) % 2 == 0)
+        return launch_persistent<128, ATTN_D128_PERSIST_SHAPE, BF16>(a, stream);
       if (!a.causal && a.N <= kShortKeys) return launch_noncausal<128, ATTN_D128_SHORT_SHAPE, BF16>(a, stream);
       return launch_modes<128, ATTN_D128_SHAPE, BF16>(a, stream);
     case 256: return launch_modes<256, ATTN_D256_SHAPE, BF16>(a, stream);

@@ -19,8 +19,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # source file -> (kernel name fragment, number of instances the dispatch builds)
 KERNELS = {
-    # bf16/fp16 x (d 64/128/256 x (4 modes + 2 windowed) + the short non-causal d = 128 shape x 2 modes)
-    "attn_fwd.hip": ("fwd_kernel", 2 * (3 * 6 + 2)),
+    # bf16/fp16 x (d 64/128/256 x (4 modes + 2 windowed) + the short non-causal d = 128 shape x 2 modes
+    # + the persistent non-causal dense d = 128 shape)
+    "attn_fwd.hip": ("fwd_kernel", 2 * (3 * 6 + 2 + 1)),
     "fp8.hip": ("fwd_fp8_kernel", 6),            # 4 modes + 2 windowed
     "attn_bwd.hip": ("bwd_", None),
 }

@@ -61,6 +61,41 @@ def test_varlen_noncausal_d128_both_loops(lengths):
     _compare_full(inp, f"varlen non-causal d=128 lengths={lengths}")
 
 
+# Dense non-causal d = 128 with at most 1024 keys and an even number of 64-key tiles runs
+# persistent workgroups (one per CU, each taking every G-th query block in turn).  B is chosen so
+# that there are more blocks than CUs (several blocks per workgroup, the last workgroups one
+# fewer), or fewer (one block each); odd tile counts (N = 576) take the per-block loops.
+@pytest.mark.parametrize("N,B,Hq,Hkv,dtype", [(512, 32, 16, 16, "bf16"), (640, 5, 24, 8, "fp16"), (1000, 3, 32, 8, "bf16"),
+                                              (1024, 2, 16, 4, "bf16"), (128, 1, 4, 2, "bf16"), (576, 4, 8, 8, "bf16")])
+def test_persistent_blocks(N, B, Hq, Hkv, dtype):
+    inp = si.dense_inputs(B, N, Hq, 128, Hkv=Hkv, causal=False, seed=930 + N, dtype=dtype)
+    _compare_full(inp, f"persistent blocks N={N} B={B} Hq={Hq} Hkv={Hkv} {dtype}")
+
+
+@pytest.mark.parametrize("N", [512, 1024])
+def test_persistent_and_per_block_loops_bit_identical(N):
+    """The persistent stream takes each block's tiles in the same order with the same arithmetic
+    as the per-block loops, so the same data given as equal packed sequences (which take the
+    plain loop at 512 keys and the ping-pong loop at 1024) must give the same bits."""
+    import torch
+
+    B, H = 6, 16
+    inp = si.dense_inputs(B, N, H, 128, causal=False, seed=940 + N)
+    gu.say("persistent vs per-block loops", N)
+    q, k, v, _ = gu.to_device(inp)
+    o1, l1 = gu.attention_nan(q, k, v, causal=False, alpha=inp.alpha)
+    cu = torch.arange(0, (B + 1) * N, N, dtype=torch.int32, device="cuda")
+    flat = [t.reshape(B * N, H, 128) for t in (q, k, v)]
+    o2, l2 = gu.attention_nan(*flat, causal=False, alpha=inp.alpha, cu_seqlens=cu, max_seqlen=N)
+    torch.cuda.synchronize()
+    o1, l1 = o1.float().cpu().numpy().reshape(B * N, H, 128), l1.cpu().numpy()
+    o2, l2 = o2.float().cpu().numpy(), l2.cpu().numpy()
+    assert np.all(np.isfinite(o1)) and np.all(np.isfinite(l1))
+    assert np.array_equal(o1, o2)
+    # LSE: dense [B, H, N], packed [H, T]
+    assert np.array_equal(l1.transpose(1, 0, 2).reshape(H, B * N), l2)
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 def test_plain_and_ping_pong_loops_bit_identical(dtype):
     """Both tile loops take the same tiles in the same key order with the same arithmetic, so
