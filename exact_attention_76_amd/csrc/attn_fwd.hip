@@ -24,7 +24,10 @@
 //     (the digest's section 3.3 idea, enforced with workgroup barriers): the two halves of the
 //     workgroup run one phase apart, so that on every SIMD one wave multiplies while the other
 //     takes its softmax; operand reads run a few products ahead of the matrix instructions,
-//     and K/V rotate through three buffers.
+//     and K/V rotate through three buffers.  Short dense non-causal d = 128 inputs run the plain
+//     loop in persistent workgroups (one per CU, each taking a fixed share of the query blocks
+//     in turn and fetching the next block's first tile and Q during the current block), the
+//     persistent scheduling the digest's section 9 names for short sequences.
 //   * exp2 with the scale alpha*log2(e) folded into one FMA per score.
 //   * Work decomposition: each XCD (dispatch is round-robin over the 8 XCDs) owns the same
 //     heads of every sequence, whole KV groups where possible, so that packed sequences of
@@ -97,6 +100,10 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
   __shared__ __attribute__((aligned(1024))) char vb0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char vb1[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char vb2[NBUF > 2 ? TILE_BYTES : 1];
+  // persistent shape: each wave's 32 rows of O, staged between blocks
+  // (placed after the K/V buffers, whose operand reads then keep addresses below 64 KB that
+  // fit the LDS instructions' immediate offsets)
+  __shared__ __attribute__((aligned(16))) char ob[SH::PERSIST ? WAVES * 32 * D * 2 : 1];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -314,6 +321,39 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
     // block sits in buffer j % 2, and the next block's tile 0 is copied into buffer 0 while the
     // current block's last tile (buffer 1) is multiplied.
     static_assert(!SH::PP && !CAUSAL && !VARLEN && !WINDOW, "persistent blocks: plain loop, non-causal, dense");
+    // A finished block's O goes out through LDS: each wave writes its 32 rows of D 16-bit values
+    // row-major into its own LDS area (the 16-byte chunks of row r at chunk ^ (r mod 16), so that
+    // both the writes and the reads back are free of bank conflicts), then stores four whole rows
+    // (1 KB of 128-byte lines) per instruction.  Straight from the accumulators, every store
+    // would touch 32 rows at 16 bytes each; those stores take longer to drain, and the next
+    // block's first copy wait waits for them.
+    constexpr int ROWB = D * 2;
+    static_assert(ROWB == 256, "the write-out assumes 16 chunks of 16 bytes per row");
+    auto finish_staged = [&]() {
+      char* const ow = ob + wave * 32 * ROWB;
+      const float lt = halves_sum(l);
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+#pragma unroll
+      for (int db = 0; db < NB_D; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const u32x2 pr = {pack2<BF16>(oacc[db][4 * gq + 0] * inv, oacc[db][4 * gq + 1] * inv),
+                            pack2<BF16>(oacc[db][4 * gq + 2] * inv, oacc[db][4 * gq + 3] * inv)};
+          *LDS_PTR(u32x2, ow + l32 * ROWB + (((4 * db + gq) ^ (l32 & 15)) * 16) + 8 * hi) = pr;
+        }
+      if (hi == 0 && qi < n) lse[((int64_t)b * Hq + h) * N + qi] = lt > 0.f ? m * alpha + __logf(lt) : -INFINITY;
+      // step t: lane (lr = lane / 16, cc = lane % 16) stores chunk cc of row r = 4t + lr, held at
+      // chunk cc ^ (r mod 16) = (cc ^ lr) ^ 4 (t mod 4) of its LDS row
+      const int lr = lane >> 4, cc = lane & 15;
+      const int src = lr * ROWB + ((cc ^ lr) * 16);
+      char* const dst = reinterpret_cast<char*>(o + (int64_t)(seq_start + qw + lr) * qstride + (int64_t)h * D) + cc * 16;
+      const int rows = min(32, n - qw);
+#pragma unroll
+      for (int t = 0; t < 32 / 4; ++t) {
+        const u32x4 x = *LDS_PTR(u32x4, ow + t * 4 * ROWB + (src ^ (64 * (t & 3))));
+        if (4 * t + lr < rows) *reinterpret_cast<u32x4*>(dst + (int64_t)t * 4 * qstride * 2) = x;
+      }
+    };
     const int G = gridDim.x;
     const int mine = (blocks - (int)blockIdx.x + G - 1) / G;
     u32x4 qn[KS_D];
@@ -339,7 +379,7 @@ __global__ __launch_bounds__(64 * SH::WAVES) void fwd_kernel(
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
       }
-      finish();
+      finish_staged();
       if (!more) return;
       // the next block becomes the current one, with a fresh online softmax
 #pragma unroll
