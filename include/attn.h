@@ -18,7 +18,9 @@
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The library allocates
- *     nothing and keeps no state between calls, so calls are thread-safe.
+ *     nothing and keeps no state between calls, so calls are thread-safe; the one exception
+ *     is attn_bwd_noalloc, whose per-GPU static workspace makes overlapping calls on one GPU
+ *     race (see there).
  *   - Work is enqueued on `stream` (NULL = the default stream) and the call returns without
  *     synchronising.  Faults of the enqueued kernels surface at the caller's next sync.
  *   - Every argument is validated before anything is enqueued: ATTN_ERR_INVALID,
