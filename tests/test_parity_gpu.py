@@ -64,9 +64,11 @@ def test_varlen_noncausal_d128_both_loops(lengths):
 # Dense non-causal d = 128 with at most 1024 keys and an even number of 64-key tiles runs
 # persistent workgroups (one per CU, each taking every G-th query block in turn).  B is chosen so
 # that there are more blocks than CUs (several blocks per workgroup, the last workgroups one
-# fewer), or fewer (one block each); odd tile counts (N = 576) take the per-block loops.
+# fewer), or fewer (one block each); odd tile counts (N = 576) take the per-block loops.  Hq = 12
+# (not a multiple of the 8 XCDs) takes the decomposition's contiguous-range branch.
 @pytest.mark.parametrize("N,B,Hq,Hkv,dtype", [(512, 32, 16, 16, "bf16"), (640, 5, 24, 8, "fp16"), (1000, 3, 32, 8, "bf16"),
-                                              (1024, 2, 16, 4, "bf16"), (128, 1, 4, 2, "bf16"), (576, 4, 8, 8, "bf16")])
+                                              (1024, 2, 16, 4, "bf16"), (128, 1, 4, 2, "bf16"), (576, 4, 8, 8, "bf16"),
+                                              (512, 16, 12, 4, "bf16")])
 def test_persistent_blocks(N, B, Hq, Hkv, dtype):
     inp = si.dense_inputs(B, N, Hq, 128, Hkv=Hkv, causal=False, seed=930 + N, dtype=dtype)
     _compare_full(inp, f"persistent blocks N={N} B={B} Hq={Hq} Hkv={Hkv} {dtype}")
