@@ -92,7 +92,7 @@ def measured_traffic(key):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--warmup-seconds", type=float, default=0.2,
                     help="keep warming up (in rounds of --warmup steps) until this much time has passed; "
