@@ -221,7 +221,7 @@ int attn_fp8_prepare_ex(const void* q, const void* k, const void* v, void* q8, v
   if (d != 128) return ATTN_ERR_UNSUPPORTED;
   if ((long long)B * Hq * ((N + 63) / 64) > 0x7fffffffLL) return ATTN_ERR_UNSUPPORTED;  // grid size
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q8) || !aligned16(k8) || !aligned16(v8) ||
-      !aligned16(rope_cos) || !aligned16(rope_sin))
+      !aligned16(rope_cos) || !aligned16(rope_sin) || !aligned16(hadamard_signs))
     return ATTN_ERR_ALIGN;
   attn::PrepareArgs a{q, k, v, q8, k8, v8, q_scale, k_scale, v_scale, B, Hq, Hkv, N, d, cu_seqlens, hadamard_signs,
                       scaling == ATTN_FP8_SCALE_TENSOR, rope_cos, rope_sin};

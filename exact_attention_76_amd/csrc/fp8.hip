@@ -103,6 +103,16 @@ __device__ __forceinline__ double quad_xor_d(double x) {
 
 // Smallest exponent of a normal fp32 scale.
 constexpr int kScaleExpMin = -126;
+// The smallest e with amax <= 448 * 2^e (0 for amax = 0): amax = f * 2^ex with f in [0.5, 1),
+// and 448 = 0.875 * 2^9.  amax is a normal fp64 (a magnitude of a bf16 value or of a sum of
+// them), so its exponent field gives ex.
+__device__ __forceinline__ int block_exponent(double amax) {
+  if (!(amax > 0.0)) return 0;
+  const long long bits = __double_as_longlong(amax);
+  const int ex = (int)((bits >> 52) & 0x7FF) - 1022;
+  const long long frac = bits & 0xFFFFFFFFFFFFFLL;  // f = (1 + frac / 2^52) / 2
+  return (frac <= (3LL << 50)) ? ex - 9 : ex - 8;
+}
 
 // What one launch of the pre-pass kernel does.
 enum PrepPass : int {
@@ -146,7 +156,7 @@ __device__ __forceinline__ void rope32(double* y, const float* __restrict__ cos_
 // first embedded at each token's position in its sequence with the fp32 tables rope_cos,
 // rope_sin [positions, 64].
 template <int PASS, bool ROPE>
-__global__ __launch_bounds__(256) void fp8_prepare_kernel(PrepTensor t0, PrepTensor t1, PrepTensor t2, int B, int N,
+__global__ __launch_bounds__(256, 4) void fp8_prepare_kernel(PrepTensor t0, PrepTensor t1, PrepTensor t2, int B, int N,
                                                           int nblk, const int* __restrict__ cu,
                                                           const signed char* __restrict__ signs,
                                                           const float* __restrict__ rope_cos,
@@ -173,19 +183,76 @@ __global__ __launch_bounds__(256) void fp8_prepare_kernel(PrepTensor t0, PrepTen
   const bool valid = token < n;
   const int64_t rowoff = ((int64_t)seq_start + (valid ? token : 0)) * H + h;
 
-  double y[32];
+  u32x4 raw[4];  // this lane's 32 bf16 values, as loaded
   {
     const u32x4* src = reinterpret_cast<const u32x4*>(t.x + rowoff * 128 + 32 * p);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const u32x4 w = valid ? src[c] : u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        y[8 * c + 2 * e] = (double)__uint_as_float(w[e] << 16);
-        y[8 * c + 2 * e + 1] = (double)__uint_as_float(w[e] & 0xFFFF0000u);
-      }
-    }
+    for (int c = 0; c < 4; ++c) raw[c] = valid ? src[c] : u32x4{0, 0, 0, 0};
   }
+  // value i (exact in fp32) of the lane's 32
+  auto bf16_at = [&](int i) {
+    const uint32_t w = raw[i >> 3][(i >> 1) & 3];
+    return __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  };
+  // Without rotation or rotary embedding (V always; Q and K when no signs are given) the values
+  // stay the bf16 inputs: exact in fp32, and so is their scaling by 2^-e except where the
+  // product falls below fp32's normal range, far under half of e4m3's smallest step (2^-10), so
+  // the nearest-even e4m3 conversion of the fp32 product gives the code of the exact value.
+  // Uniform per workgroup.
+  auto narrow_path = [&]() {
+    int e;
+    if constexpr (PASS == kPrepTensorCodes) {
+      e = (int)((__float_as_uint(*slot) >> 23) & 0xFF) - 127 + t.scale_shift;
+    } else {
+      float amax = 0.f;
+      if (valid) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(bf16_at(i)));
+      }
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+      __shared__ float wmaxf[4];
+      if ((tid & 63) == 0) wmaxf[tid >> 6] = amax;
+      __syncthreads();
+      amax = fmaxf(fmaxf(wmaxf[0], wmaxf[1]), fmaxf(wmaxf[2], wmaxf[3]));
+      e = block_exponent((double)amax);
+      if constexpr (PASS == kPrepTensorScan) {
+        if (tid == 0) *slot = __int_as_float(amax > 0.f ? e : INT_MIN);
+        return;
+      }
+      e = max(e, t.scale_shift + kScaleExpMin);
+    }
+    // 2^-e as fp32: e lies in [kScaleExpMin + shift, 128] here, so 2^-e is a normal fp32
+    const float inv = __uint_as_float((uint32_t)(127 - e) << 23);
+    if (valid) {
+      uint32_t w[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        // fma(x, 2^-e, +0): the exact product, an exact -0 turned into +0 (a zero encodes as +0)
+        const float f0 = __builtin_fmaf(bf16_at(4 * j), inv, 0.0f);
+        const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f0, __builtin_fmaf(bf16_at(4 * j + 1), inv, 0.0f), __float_as_int(f0), false);
+        w[j] = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_fmaf(bf16_at(4 * j + 2), inv, 0.0f),
+                                               __builtin_fmaf(bf16_at(4 * j + 3), inv, 0.0f), lo, true);
+      }
+      u32x4* dst = reinterpret_cast<u32x4*>(t.x8 + rowoff * 128 + 32 * p);
+      dst[0] = u32x4{w[0], w[1], w[2], w[3]};
+      dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+    }
+    if constexpr (PASS == kPrepBlock) {
+      if (tid == 0) *slot = __uint_as_float((uint32_t)(e - t.scale_shift + 127) << 23);
+    }
+  };
+  // (the test reads an opaque copy of the rotate flag: knowing the flag set on the path below,
+  // the compiler merged that path into one scheduling region that held twice the registers)
+  int rotate = t.rotate;
+  asm volatile("" : "+s"(rotate));
+  if (!rotate && !(ROPE && t.embed)) {
+    narrow_path();
+    return;
+  }
+  double y[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) y[i] = (double)bf16_at(i);
   if constexpr (ROPE) {
     if (t.embed) {
       const int64_t row = (int64_t)(valid ? token : 0) * 64 + 16 * p;
@@ -193,9 +260,18 @@ __global__ __launch_bounds__(256) void fp8_prepare_kernel(PrepTensor t0, PrepTen
     }
   }
   if (t.rotate) {
+    {
+      // this lane's 32 sign bytes as two 16-byte words (each +1 or -1: bit 7 is the sign),
+      // applied to the doubles' sign bits
+      const u32x4* sp = reinterpret_cast<const u32x4*>(signs + 32 * p);
+      const u32x4 s0 = sp[0], s1 = sp[1];
 #pragma unroll
-    for (int i = 0; i < 32; ++i)
-      if (signs[32 * p + i] < 0) y[i] = -y[i];
+      for (int i = 0; i < 32; ++i) {
+        const uint32_t word = (i < 16 ? s0 : s1)[(i & 15) >> 2];
+        const uint32_t neg = (word >> (8 * (i & 3) + 7)) & 1u;
+        y[i] = __longlong_as_double(__double_as_longlong(y[i]) ^ ((long long)neg << 63));
+      }
+    }
     // Walsh-Hadamard butterflies (a, b) -> (a + b, a - b) at strides 1 .. 64 over the 128
     // features give y H with H[i][j] = (-1)^popcount(i & j); strides below 32 stay in a lane.
 #pragma unroll
@@ -212,8 +288,13 @@ __global__ __launch_bounds__(256) void fp8_prepare_kernel(PrepTensor t0, PrepTen
     // same as the add or subtract.
     auto cross = [&](auto xchg, int m) {
       const double sg = (p & m) ? -1.0 : 1.0;
+      // eight values at a time, so that the partner values of all 32 are not held at once
 #pragma unroll
-      for (int i = 0; i < 32; ++i) y[i] = __builtin_fma(sg, y[i], xchg(y[i]));
+      for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int i = 8 * c; i < 8 * c + 8; ++i) y[i] = __builtin_fma(sg, y[i], xchg(y[i]));
+        __builtin_amdgcn_sched_barrier(0);
+      }
     };
     cross([](double x) { return quad_xor_d<1>(x); }, 1);
     cross([](double x) { return quad_xor_d<2>(x); }, 2);
@@ -234,14 +315,7 @@ __global__ __launch_bounds__(256) void fp8_prepare_kernel(PrepTensor t0, PrepTen
     if ((tid & 63) == 0) wmax[tid >> 6] = amax;
     __syncthreads();
     amax = fmax(fmax(wmax[0], wmax[1]), fmax(wmax[2], wmax[3]));
-    // smallest e with amax <= 448 * 2^e: amax = f * 2^ex, f in [0.5, 1); 448 = 0.875 * 2^9
-    e = 0;
-    if (amax > 0.0) {
-      const long long bits = __double_as_longlong(amax);
-      const int ex = (int)((bits >> 52) & 0x7FF) - 1022;
-      const long long frac = bits & 0xFFFFFFFFFFFFFLL;  // f = (1 + frac / 2^52) / 2
-      e = (frac <= (3LL << 50)) ? ex - 9 : ex - 8;
-    }
+    e = block_exponent(amax);
     if constexpr (PASS == kPrepTensorScan) {
       if (tid == 0) *slot = __int_as_float(amax > 0.0 ? e : INT_MIN);
       return;

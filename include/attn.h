@@ -187,7 +187,7 @@ int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
  * requires).
  *
  * Inputs q [B, N, Hq, d], k and v [B, N, Hkv, d], bf16, dense layout, d = 128.
- * If hadamard_signs (device int8 [d], each +1 or -1) is non-NULL, q and k are first
+ * If hadamard_signs (device int8 [d], each +1 or -1, 16-byte aligned) is non-NULL, q and k are first
  * multiplied along d by D H, where D = diag(signs) and H is the unnormalised Sylvester
  * Hadamard matrix (entries +-1); v is never rotated.  NULL skips the rotation.
  * Then, per (batch, head, block of 64 tokens), with amax the largest magnitude in the

@@ -102,10 +102,10 @@ def test_fwd_window_validation(lib, window, kw, status):
     assert fwd_window(lib, window, **kw) == status
 
 
-def prep(lib, q=A, k=A, v=A, q8=A, k8=A, v8=A, qs=A, ks=A, vs=A, B=1, Hq=2, Hkv=2, N=128, d=128):
+def prep(lib, q=A, k=A, v=A, q8=A, k8=A, v8=A, qs=A, ks=A, vs=A, B=1, Hq=2, Hkv=2, N=128, d=128, signs=None):
     P = ctypes.c_void_p
     return lib.attn_fp8_prepare(P(q), P(k), P(v), P(q8), P(k8), P(v8), P(qs), P(ks), P(vs),
-                                B, Hq, Hkv, N, d, None, None)
+                                B, Hq, Hkv, N, d, P(signs) if signs else None, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -117,6 +117,7 @@ def prep(lib, q=A, k=A, v=A, q8=A, k8=A, v8=A, qs=A, ks=A, vs=A, B=1, Hq=2, Hkv=
     (dict(d=64), ea.ATTN_ERR_UNSUPPORTED),
     (dict(q8=A + 1), ea.ATTN_ERR_ALIGN),
     (dict(k=A + 2), ea.ATTN_ERR_ALIGN),
+    (dict(signs=A + 8), ea.ATTN_ERR_ALIGN),  # the signs are read as 16-byte words
 ])
 def test_prepare_validation(lib, kw, status):
     assert prep(lib, **kw) == status
