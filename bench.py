@@ -68,10 +68,10 @@ MEASURED_TRAFFIC = {
     "bf16_mha16k": {"sources": {"exact_attention_76_amd/csrc/attn_fwd.hip": "a5caee0bd4413070",
                                 _DEC: "2521a203b68b3442", _T16: "91339639cbec1225"},
                     "bytes": 403968001},
-    "fp8_attention": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "7b57f8130a1f7ca0",
-                                  _DEC: "2521a203b68b3442"}, "bytes": 185918981},
-    "fp8_prepare": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "7b57f8130a1f7ca0"},
-                    "bytes": 302628740},
+    "fp8_attention": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "42bf6866be33abb5",
+                                  _DEC: "2521a203b68b3442"}, "bytes": 185858065},
+    "fp8_prepare": {"sources": {"exact_attention_76_amd/csrc/fp8.hip": "42bf6866be33abb5"},
+                    "bytes": 302757444},
 }
 
 
