@@ -21,6 +21,10 @@
 //     column; per key tile S^T = K Q^T and dP^T = V dO^T, dS^T in registers, dQ^T += K^T dS^T
 //     with K read transposed.  Every gradient is written once; no atomics, so the result is
 //     deterministic.
+//   * In both kernels a tile's products run as two streams (the first products, then the
+//     products with P and dS) whose LDS operands are read two to four products ahead in an order
+//     pinned for the scheduler; the first operands of the second stream are read before the
+//     softmax.  The masks of edge tiles stay behind a branch.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -105,50 +109,6 @@ __device__ __forceinline__ void operand_offsets(int lane, int* koff, int* vtoff)
   }
 }
 
-// C (32 x 32 per block cb) += tile rows (32*cb ..) x frag: one block per 32 tile rows.
-template <int D, bool BF16, int NB>
-__device__ __forceinline__ void rows_product(const char* tile, const int* koff, const u32x4* frag, f32x16* acc) {
-  constexpr int NCH = D / 8, KS_D = D / 16;
-#pragma unroll
-  for (int cb = 0; cb < NB; ++cb) {
-    acc[cb] = f32x16{};
-#pragma unroll
-    for (int st = 0; st < KS_D; ++st) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(tile + koff[st & 1] + cb * 512 * NCH + 512 * (st & ~1));
-      acc[cb] = mma32<BF16>(a, frag[st], acc[cb]);
-    }
-  }
-}
-
-// acc (32 x 32) = tile rows (32 ..) x the B operand read, k-step by k-step, from row block
-// `brow` (32 rows) of another tile in the same layout: one product whose both operands are in LDS.
-template <int D, bool BF16>
-__device__ __forceinline__ void rows_product_lds(const char* tile, const int* koff, const char* btile, int brow,
-                                                 f32x16& acc) {
-  constexpr int NCH = D / 8, KS_D = D / 16;
-  acc = f32x16{};
-#pragma unroll
-  for (int st = 0; st < KS_D; ++st) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(tile + koff[st & 1] + 512 * (st & ~1));
-    const u32x4 b = *reinterpret_cast<const u32x4*>(btile + koff[st & 1] + brow * 512 * NCH + 512 * (st & ~1));
-    acc = mma32<BF16>(a, b, acc);
-  }
-}
-
-// acc^T (D x 32) += tile^T (D x 16 rows of k-step st) x pf: the transposed product of one k-step.
-template <int D, bool BF16>
-__device__ __forceinline__ void tr_product_step(const char* tile, const int* vtoff, int st, u32x4 pf, f32x16* acc) {
-  constexpr int NCH = D / 8, NB_D = D / 32;
-#pragma unroll
-  for (int db = 0; db < NB_D; ++db) {
-    const int imm = st * 256 * NCH + db * 1024;
-    const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, tile + vtoff[0] + imm));
-    const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, tile + vtoff[1] + imm));
-    const u32x2 a0 = __builtin_bit_cast(u32x2, t0), a1 = __builtin_bit_cast(u32x2, t1);
-    acc[db] = mma32<BF16>(u32x4{a0[0], a0[1], a1[0], a1[1]}, pf, acc[db]);
-  }
-}
-
 // k-step st of a 32-row accumulator block pair, packed as the B operand (registers 8*(st%2) ..
 // of block st/2).
 template <bool BF16>
@@ -156,6 +116,57 @@ __device__ __forceinline__ u32x4 pack_step(const f32x16* x, int st) {
   const int cb = st >> 1, base = (st & 1) * 8;
   return u32x4{pack2<BF16>(x[cb][base + 0], x[cb][base + 1]), pack2<BF16>(x[cb][base + 2], x[cb][base + 3]),
                pack2<BF16>(x[cb][base + 4], x[cb][base + 5]), pack2<BF16>(x[cb][base + 6], x[cb][base + 7])};
+}
+
+// A stream of N products whose operands come from LDS, each read PD products ahead of its
+// matrix instruction: read(i) returns operand i, product(i, a) issues product i, and pin(i)
+// names the LDS reads of operand i for the scheduler.  Without the pinned order the compiler
+// reads each operand right before its product, and every matrix instruction waits the full
+// LDS latency.  With PRIMED the first PD operands are already in `win` (read by prime()).
+template <int N, int PD, bool PRIMED, class T, class Read, class Product, class Pin>
+__device__ __forceinline__ void product_stream(Read read, Product product, Pin pin, T* win) {
+  if constexpr (!PRIMED) {
+#pragma unroll
+    for (int i = 0; i < PD; ++i) win[i] = read(i);
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const T a = win[i % PD];
+    if (i + PD < N) win[i % PD] = read(i + PD);
+    product(i, a);
+  }
+  if constexpr (!PRIMED) {
+#pragma unroll
+    for (int i = 0; i < PD; ++i) pin(i);
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i + PD < N) pin(i + PD);
+  }
+}
+template <int PD, class T, class Read>
+__device__ __forceinline__ void prime(Read read, T* win) {
+#pragma unroll
+  for (int i = 0; i < PD; ++i) win[i] = read(i);
+}
+// scheduler pins for operands of one and of two LDS reads
+struct Pin1 {
+  __device__ void operator()(int) const { __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); }
+};
+struct Pin2 {
+  __device__ void operator()(int) const { __builtin_amdgcn_sched_group_barrier(0x100, 2, 0); }
+};
+
+// Transposed operand (D rows of 16 tile rows, k-step st, d block db) by two ds_read_b64_tr_b16.
+template <int D>
+__device__ __forceinline__ u32x4 tr_operand(const char* tile, const int* vtoff, int st, int db) {
+  constexpr int NCH = D / 8;
+  const int imm = st * 256 * NCH + db * 1024;
+  const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, tile + vtoff[0] + imm));
+  const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, tile + vtoff[1] + imm));
+  const u32x2 a0 = __builtin_bit_cast(u32x2, t0), a1 = __builtin_bit_cast(u32x2, t1);
+  return u32x4{a0[0], a0[1], a1[0], a1[1]};
 }
 
 // Accumulator row held by register r of a 32x32 block: 8*(r/4) + 4*hi + r%4.
@@ -298,6 +309,9 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(
   f32x16 dka[NB_D], dva[NB_D];
 #pragma unroll
   for (int i = 0; i < NB_D; ++i) dka[i] = dva[i] = f32x16{};
+  // read-ahead of the two product streams (operands of two dP products fill as many registers
+  // as four of the others)
+  constexpr int PD1 = 2, PD2 = 4;
   const float c = alpha * kLog2e;
 
   auto compute = [&](const char* qt, const char* gt, float (*ldt)[256], int s) {
@@ -305,39 +319,95 @@ __global__ __launch_bounds__(64 * kKvWaves, 1) void bwd_dkdv_kernel(
     if (CAUSAL && q0 + TQ - 1 < kw) return;  // every query of the tile is before this wave's keys
     if (WINDOW && q0 > kw + 31 + window - 1) return;  // every query is past this wave's windows
     f32x16 sc[NB], dp[NB];
-    rows_product<D, BF16, NB>(qt, koff, kf, sc);  // S = Q K^T (rows: queries; column: this lane's key)
-    if constexpr (V_LDS) rows_product_lds<D, BF16>(gt, koff, vres, wave, dp[0]);  // dP = dO V^T
-    else rows_product<D, BF16, NB>(gt, koff, vf, dp);
-    const bool mask = (q0 + TQ > n) || (CAUSAL && q0 < kw + 31) || (WINDOW && q0 + TQ - 1 > kw + window - 1);
+    // first stage, products 0 .. NP-1: S = Q K^T (rows: queries; column: this lane's key), NP ..
+    // 2NP-1: dP = dO V^T (V from the workgroup's LDS rows at d = 128, else from registers);
+    // each 32-query block's k-steps in order
+    constexpr int NP = NB * KS_D;
+    struct Op2 {
+      u32x4 a, b;
+    };
+    auto read1 = [&](int i) -> Op2 {
+      const int ii = i % NP, cb = ii % NB, st = ii / NB;
+      const char* t = i < NP ? qt : gt;
+      const u32x4 a = *reinterpret_cast<const u32x4*>(t + koff[st & 1] + cb * 512 * NCH + 512 * (st & ~1));
+      if (V_LDS && i >= NP)
+        return Op2{a, *reinterpret_cast<const u32x4*>(vres + koff[st & 1] + wave * 512 * NCH + 512 * (st & ~1))};
+      return Op2{a, u32x4{}};
+    };
+    auto product1 = [&](int i, Op2 o) {
+      const int ii = i % NP, cb = ii % NB, st = ii / NB;
+      if (i < NP) {
+        sc[cb] = mma32<BF16>(o.a, kf[st], st == 0 ? f32x16{} : sc[cb]);
+      } else {
+        if constexpr (V_LDS) dp[cb] = mma32<BF16>(o.a, o.b, st == 0 ? f32x16{} : dp[cb]);
+        else dp[cb] = mma32<BF16>(o.a, vf[st], st == 0 ? f32x16{} : dp[cb]);
+      }
+    };
+    auto pin1 = [](int i) {
+      if (V_LDS && i >= NP) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      else __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    };
+    Op2 win1[PD1];
+    product_stream<2 * NP, PD1, false>(read1, product1, pin1, win1);
+    __builtin_amdgcn_sched_barrier(0);
+    // second stage: per k-step st, dV^T += dO^T P over the d blocks, then dK^T += Q^T dS; the
+    // first PD2 operands are read before the softmax
+    auto read2 = [&](int i) {
+      const int st = i / (2 * NB_D), w = i % (2 * NB_D);
+      return tr_operand<D>(w < NB_D ? gt : qt, vtoff, st, w % NB_D);
+    };
+    u32x4 win2[PD2];
+    prime<PD2>(read2, win2);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * PD2, 0);
+    // P = exp(S - L) (the query of each accumulator row picks its L and D from LDS)
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const int row0 = 32 * cb + 8 * r4 + 4 * hi;  // four consecutive queries of this register group
-        const float4 L = *reinterpret_cast<const float4*>(&ldt[0][row0]);
-        const float4 Dv = *reinterpret_cast<const float4*>(&ldt[1][row0]);
-        const float Lr[4] = {L.x, L.y, L.z, L.w}, Dr[4] = {Dv.x, Dv.y, Dv.z, Dv.w};
+        const float4 L = *reinterpret_cast<const float4*>(&ldt[0][32 * cb + 8 * r4 + 4 * hi]);
+        const float Lr[4] = {L.x, L.y, L.z, L.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * r4 + e;
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cb][r], c, -Lr[e] * kLog2e));
-          if (mask) {
-            const int qi = q0 + row0 + e;
-            if constexpr (WINDOW) {  // visible iff 0 <= qi - kj < window
-              if (qi >= n || (unsigned)(qi - kj) >= (unsigned)window) p = 0.f;
-            } else {
-              if (qi >= n || (CAUSAL && qi < kj)) p = 0.f;
-            }
-          }
-          sc[cb][r] = p;
-          dp[cb][r] = p * (dp[cb][r] - Dr[e]);
-        }
+        for (int e = 0; e < 4; ++e)
+          sc[cb][4 * r4 + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cb][4 * r4 + e], c, -Lr[e] * kLog2e));
       }
+    const bool mask = (q0 + TQ > n) || (CAUSAL && q0 < kw + 31) || (WINDOW && q0 + TQ - 1 > kw + window - 1);
+    if (mask) {
+      asm volatile("");  // keeps the edge tiles' masking a branch (not selects on every tile)
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = q0 + 32 * cb + acc_row(r, hi);
+          if constexpr (WINDOW) {  // visible iff 0 <= qi - kj < window
+            if (qi >= n || (unsigned)(qi - kj) >= (unsigned)window) sc[cb][r] = 0.f;
+          } else {
+            if (qi >= n || (CAUSAL && qi < kj)) sc[cb][r] = 0.f;
+          }
+        }
+    }
+    // dS = P (dP - D)
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float4 Dv = *reinterpret_cast<const float4*>(&ldt[1][32 * cb + 8 * r4 + 4 * hi]);
+        const float Dr[4] = {Dv.x, Dv.y, Dv.z, Dv.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dp[cb][4 * r4 + e] = sc[cb][4 * r4 + e] * (dp[cb][4 * r4 + e] - Dr[e]);
+      }
+    u32x4 pv[KS], pk[KS];
 #pragma unroll
     for (int st = 0; st < KS; ++st) {
-      tr_product_step<D, BF16>(gt, vtoff, st, pack_step<BF16>(sc, st), dva);  // dV^T += dO^T P
-      tr_product_step<D, BF16>(qt, vtoff, st, pack_step<BF16>(dp, st), dka);  // dK^T += Q^T dS
+      pv[st] = pack_step<BF16>(sc, st);
+      pk[st] = pack_step<BF16>(dp, st);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    auto product2 = [&](int i, u32x4 a) {
+      const int st = i / (2 * NB_D), w = i % (2 * NB_D);
+      if (w < NB_D) dva[w] = mma32<BF16>(a, pv[st], dva[w]);
+      else dka[w - NB_D] = mma32<BF16>(a, pk[st], dka[w - NB_D]);
+    };
+    product_stream<KS * 2 * NB_D, PD2, true>(read2, product2, Pin2{}, win2);
   };
 
   issue(qt0, gt0, ld0, 0);
@@ -462,26 +532,59 @@ __global__ __launch_bounds__(64 * kWaves, 2) void bwd_dq_kernel(
     if (CAUSAL && j0 > qw + 31) return;  // the tile lies wholly after this wave's queries
     if (WINDOW && j0 + kTile - 1 <= qw - window) return;  // wholly before this wave's windows
     f32x16 sc[NB], dp[NB];
-    rows_product<D, BF16, NB>(kt, koff, qf, sc);  // S^T = K Q^T (rows: keys; column: this lane's query)
-    rows_product<D, BF16, NB>(vt, koff, gf, dp);  // dP^T = V dO^T
-    const bool mask = (j0 + kTile > n) || (CAUSAL && j0 + kTile - 1 > qw) || (WINDOW && j0 <= qw + 31 - window);
+    // products 0 .. NP-1: S^T = K Q^T (rows: keys; column: this lane's query), NP .. 2NP-1:
+    // dP^T = V dO^T; the 32-key blocks alternate, each block's k-steps in order
+    constexpr int NP = NB * KS_D, PD1 = 4, PD2 = 4;
+    auto read1 = [&](int i) {
+      const char* t = i < NP ? kt : vt;
+      const int ii = i % NP, cb = ii % NB, st = ii / NB;
+      return *reinterpret_cast<const u32x4*>(t + koff[st & 1] + cb * 512 * NCH + 512 * (st & ~1));
+    };
+    auto product1 = [&](int i, u32x4 a) {
+      const int ii = i % NP, cb = ii % NB, st = ii / NB;
+      if (i < NP) sc[cb] = mma32<BF16>(a, qf[st], st == 0 ? f32x16{} : sc[cb]);
+      else dp[cb] = mma32<BF16>(a, gf[st], st == 0 ? f32x16{} : dp[cb]);
+    };
+    u32x4 win[PD1 > PD2 ? PD1 : PD2];
+    product_stream<2 * NP, PD1, false>(read1, product1, Pin1{}, win);
+    __builtin_amdgcn_sched_barrier(0);
+    // dQ^T += K^T dS^T: product i is k-step i / NB_D of d block i % NB_D, its operand K read
+    // transposed (two reads); the first PD2 are read before the softmax below
+    auto read2 = [&](int i) { return tr_operand<D>(kt, vtoff, i / NB_D, i % NB_D); };
+    prime<PD2>(read2, win);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * PD2, 0);
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cb][r], c, -Lc));
-        if (mask) {
+      for (int r = 0; r < 16; ++r) sc[cb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cb][r], c, -Lc));
+    const bool mask = (j0 + kTile > n) || (CAUSAL && j0 + kTile - 1 > qw) || (WINDOW && j0 <= qw + 31 - window);
+    if (mask) {
+      asm volatile("");  // keeps the edge tiles' masking a branch (not selects on every tile)
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
           const int key = j0 + 32 * cb + acc_row(r, hi);
           if constexpr (WINDOW) {  // visible iff 0 <= qi - key < window
-            if (key >= n || (unsigned)(qi - key) >= (unsigned)window) p = 0.f;
+            if (key >= n || (unsigned)(qi - key) >= (unsigned)window) sc[cb][r] = 0.f;
           } else {
-            if (key >= n || (CAUSAL && key > qi)) p = 0.f;
+            if (key >= n || (CAUSAL && key > qi)) sc[cb][r] = 0.f;
           }
         }
-        dp[cb][r] = p * (dp[cb][r] - Dq);
-      }
+    }
 #pragma unroll
-    for (int st = 0; st < KS; ++st) tr_product_step<D, BF16>(kt, vtoff, st, pack_step<BF16>(dp, st), dqa);
+    for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[cb][r] = sc[cb][r] * (dp[cb][r] - Dq);
+    u32x4 ds[KS];
+#pragma unroll
+    for (int st = 0; st < KS; ++st) ds[st] = pack_step<BF16>(dp, st);
+    __builtin_amdgcn_sched_barrier(0);
+    auto product2 = [&](int i, u32x4 a) {
+      const int st = i / NB_D, db = i % NB_D;
+      dqa[db] = mma32<BF16>(a, ds[st], dqa[db]);
+    };
+    product_stream<KS * NB_D, PD2, true>(read2, product2, Pin2{}, win);
   };
 
   issue(kt0, vt0, 0);
