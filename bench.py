@@ -38,9 +38,10 @@ the graphics clock the power-management firmware reports while the same launch r
 back for 2.5 s after the timed region, with the dense peak recomputed at that clock.
 
 The default line also carries, in config.workloads, every other workload timed the same way
-(the smallest one, the causal head dims, the packed causal GQA workload, and FP8 attention
-with its pre-pass and where it stands against the FP8 accuracy bar), and config.targets: the
-bf16 and FP8 fractions of peak against their goals.
+(the smallest one, the causal head dims, the packed causal GQA workload, FP8 attention
+with its pre-pass and where it stands against the FP8 accuracy bar, and the backward pass on
+the headline and causal d=128 inputs), and config.targets: the bf16 and FP8 fractions of peak
+against their goals.
 """
 from __future__ import annotations
 
@@ -534,6 +535,9 @@ def main():
                 workloads[n] = summary(run_16bit(args, n, si.CONFIGS[n](), dev, stream, oracle_s=args.oracle_seconds))
             r8 = run_fp8(args, dev, stream, "fp8", oracle_s=args.oracle_seconds, clock=True)
             workloads["fp8_b2_h16_n8192_d128"] = summary(r8)
+            # the backward pass on the headline and the causal d=128 inputs (2.5 x forward FLOPs)
+            for n in ("mha_n16384_b1_h16_d128", "causal_b2_h16_n8192_d128"):
+                workloads["bwd_" + n] = summary(run_bwd(args, "bwd_" + n, si.CONFIGS[n](), dev, stream))
             head["config"]["workloads"] = workloads
             head["config"]["targets"] = {
                 "bf16_headline_pct_of_peak": {"target": 60.0, "measured": head["config"]["pct_of_peak"]},
