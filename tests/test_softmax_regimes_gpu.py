@@ -18,9 +18,23 @@ their partial sums when it grows (the FlashAttention-3 digest, section 3: online
   A falling ramp (R = 200) puts the maximum in the first tile and drives later weights below
   fp32's range.
 
+* the scale alpha: every other test passes 1/sqrt(d), which a kernel that took its scale from d
+  instead of the argument would also pass; here alpha is 0.37, 1.0 (sharp rows) or 0.02 (nearly
+  uniform rows), through the forward (16-bit and FP8, dense, packed and windowed) and the
+  backward, where alpha also scales dQ and dK.  Sharper rows than the standard workload's
+  make the 1e-2 max-abs bar (set for alpha = 1/sqrt(d)) the wrong yardstick: the kernels round
+  the weights P to the input format before the second product, with L summed from the unrounded
+  weights, so an element of O may move by up to u * sum_j p_j |V_jc| (u = 2^-8 for bf16, 2^-11
+  for fp16: half a unit in the last place, relative), about 0.016 for a row held by one
+  |V| = 4 key.  These cases hold every element to that bound (the oracle computes the sum as
+  attention over |V|) plus half a unit in the last place of O and 1e-4 for the fp32 scores;
+  RMSE and L keep their bars.
+
 16-bit cases are held to the bars of tests/test_parity_gpu.py on every element, FP8 cases to
 the kernel's own-error bounds of tests/test_fp8_gpu.py, backward cases to the per-element
 bounds of tests/test_backward_gpu.py."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -180,4 +194,82 @@ def test_backward_regimes(case, causal, d):
     what = f"bwd {case} d={d} causal={causal}"
     gu.say(what)
     do = si.output_gradient(inp, 77)
+    check_grads(inp, do, run_gpu_bwd(inp, do), what)
+
+
+class _Scaled(si.AttnInputs):
+    """Seeded inputs whose softmax scale is meta["alpha"] rather than 1/sqrt(d)."""
+
+    @property
+    def alpha(self) -> float:
+        return float(self.meta["alpha"])
+
+
+def scaled(inp, alpha):
+    out = _Scaled(**{f.name: getattr(inp, f.name) for f in dataclasses.fields(inp)})
+    out.meta = dict(inp.meta, alpha=alpha)
+    return out
+
+
+ALPHAS = [0.37, 1.0, 0.02]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("alpha", ALPHAS)
+@pytest.mark.parametrize("layout", ["dense", "dense_causal", "packed_causal", "window"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_softmax_scale(d, dtype, layout, alpha):
+    if layout == "packed_causal":
+        inp = si.varlen_inputs([300, 0, 517, 64], 4, 2, d, causal=True, seed=d + 5, dtype=dtype)
+    else:
+        inp = si.dense_inputs(2, 333, 4, d, Hkv=2, causal=layout != "dense", seed=d + 6, dtype=dtype)
+        if layout == "window":
+            inp.window = 100
+    inp = scaled(inp, alpha)
+    what = f"alpha={alpha} d={d} {dtype} {layout}"
+    gu.say(what)
+    o, lse = gu.run_gpu(inp)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), "rows left unwritten"
+    o_ref, lse_ref = gu.oracle_full(inp)
+    q, k, v = gu.widened(inp)
+    o_absv, _ = oracle.attention(q, k, np.abs(v), causal=inp.causal, alpha=inp.alpha, cu_seqlens=inp.cu_seqlens,
+                                 window=inp.window)
+    u = {"bf16": 2.0 ** -8, "fp16": 2.0 ** -11}[inp.dtype]
+    bound = u * o_absv + gu.half_ulp(o_ref, inp.dtype) + 1e-4
+    excess = float(np.max(np.abs(o - o_ref) - bound))
+    gu.say(what, "largest error beyond the per-element bound", excess)
+    assert excess <= 0.0, (what, excess)
+    gu.check(gu.metrics(o, o_ref, lse, lse_ref, inp.dtype), max_abs=np.inf, what=what)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("alpha", ALPHAS)
+@pytest.mark.parametrize("layout", ["dense", "packed_causal"])
+def test_fp8_softmax_scale(layout, alpha):
+    if layout == "packed_causal":
+        inp = si.varlen_inputs([300, 0, 517, 64], 4, 2, 128, causal=True, seed=15)
+    else:
+        inp = si.dense_inputs(2, 333, 4, 128, Hkv=2, seed=16)
+    inp = scaled(inp, alpha)
+    gu.say("fp8 alpha", alpha, layout)
+    o, lse, prep = gpu_fp8_attention(inp, si.hadamard_signs(128, seed=55))
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), "rows left unwritten"
+    Z, own = _own_error(inp, o, lse, prep, *_all_rows(inp))
+    check_own(Z, own)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("alpha", ALPHAS)
+@pytest.mark.parametrize("layout", ["dense", "dense_causal", "packed_causal"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_softmax_scale(d, layout, alpha):
+    if layout == "packed_causal":
+        inp = si.varlen_inputs([200, 0, 333, 64], 4, 2, d, causal=True, seed=d + 7)
+    else:
+        inp = si.dense_inputs(2, 257, 4, d, Hkv=2, causal=layout != "dense", seed=d + 8)
+    inp = scaled(inp, alpha)
+    what = f"bwd alpha={alpha} d={d} {layout}"
+    gu.say(what)
+    do = si.output_gradient(inp, 78)
     check_grads(inp, do, run_gpu_bwd(inp, do), what)
