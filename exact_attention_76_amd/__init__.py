@@ -248,21 +248,24 @@ def attention(q, k, v, *, causal: bool = False, alpha: float | None = None, cu_s
               max_seqlen: int | None = None, q_scale=None, k_scale=None, v_scale=None, window: int | None = None,
               stream=None):
     """Allocate O (bf16, or fp16 for fp16 inputs) and LSE (fp32) and call :func:`attn_fwd`, or,
-    with ``window``, :func:`attn_fwd_window` (causal sliding window; ``causal`` is then implied)."""
-    out_dtype = torch.float16 if q.dtype == torch.float16 else torch.bfloat16
-    o = torch.empty(q.shape, dtype=out_dtype, device=q.device)
-    if cu_seqlens is None:
-        B, N, Hq, _ = q.shape
-        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    else:
-        T, Hq, _ = q.shape
-        lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
-    kw = dict(alpha=alpha, cu_seqlens=cu_seqlens, max_seqlen=max_seqlen, q_scale=q_scale, k_scale=k_scale,
-              v_scale=v_scale, stream=stream)
-    if window is not None:
-        attn_fwd_window(q, k, v, o, lse, window=window, **kw)
-    else:
-        attn_fwd(q, k, v, o, lse, causal=causal, **kw)
+    with ``window``, :func:`attn_fwd_window` (causal sliding window; ``causal`` is then implied).
+    The outputs are allocated on ``stream`` (default: the current stream), the stream the
+    kernel writes them on, so torch's caching allocator orders their reuse behind it."""
+    with torch.cuda.stream(stream):
+        out_dtype = torch.float16 if q.dtype == torch.float16 else torch.bfloat16
+        o = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+        if cu_seqlens is None:
+            B, N, Hq, _ = q.shape
+            lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+        else:
+            T, Hq, _ = q.shape
+            lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+        kw = dict(alpha=alpha, cu_seqlens=cu_seqlens, max_seqlen=max_seqlen, q_scale=q_scale, k_scale=k_scale,
+                  v_scale=v_scale, stream=stream)
+        if window is not None:
+            attn_fwd_window(q, k, v, o, lse, window=window, **kw)
+        else:
+            attn_fwd(q, k, v, o, lse, causal=causal, **kw)
     return o, lse
 
 
@@ -318,15 +321,19 @@ def attn_bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, *, causal: bool = False,
 
 def attention_backward(q, k, v, o, lse, dout, *, causal: bool = False, alpha: float | None = None, cu_seqlens=None,
                        max_seqlen: int | None = None, window: int | None = None, stream=None):
-    """Allocate dq, dk, dv and the workspace and call :func:`attn_bwd`."""
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    if cu_seqlens is None:
-        B, N, Hq = q.shape[0], q.shape[1], q.shape[2]
-    else:
-        B, N, Hq = cu_seqlens.numel() - 1, int(max_seqlen), q.shape[1]
-    ws = torch.empty(B * Hq * N, dtype=torch.float32, device=q.device)
-    attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, causal=causal, alpha=alpha, cu_seqlens=cu_seqlens,
-             max_seqlen=max_seqlen, window=window, stream=stream)
+    """Allocate dq, dk, dv and the workspace and call :func:`attn_bwd`.  Everything is allocated
+    on ``stream`` (default: the current stream), where the kernels run: the workspace is freed
+    on return while they may still be running, and the allocator then hands its memory only to
+    later work on that stream."""
+    with torch.cuda.stream(stream):
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        if cu_seqlens is None:
+            B, N, Hq = q.shape[0], q.shape[1], q.shape[2]
+        else:
+            B, N, Hq = cu_seqlens.numel() - 1, int(max_seqlen), q.shape[1]
+        ws = torch.empty(B * Hq * N, dtype=torch.float32, device=q.device)
+        attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, ws, causal=causal, alpha=alpha, cu_seqlens=cu_seqlens,
+                 max_seqlen=max_seqlen, window=window, stream=stream)
     return dq, dk, dv
 
 
@@ -422,7 +429,15 @@ def fp8_prepare(q, k, v, *, hadamard_signs=None, per_tensor: bool = False, cu_se
                 max_seqlen: int | None = None, rope_cos=None, rope_sin=None, stream=None):
     """Allocate the e4m3 tensors (as uint8 codes) and scales and run the pre-pass, with one scale
     per 64-token block (:func:`attn_fp8_prepare`) or, with ``per_tensor``, one per tensor;
-    ``cu_seqlens`` / ``max_seqlen`` select the packed layout (:func:`attn_fp8_prepare_ex`)."""
+    ``cu_seqlens`` / ``max_seqlen`` select the packed layout (:func:`attn_fp8_prepare_ex`).
+    The outputs are allocated on ``stream`` (default: the current stream), where the pre-pass
+    writes them."""
+    with torch.cuda.stream(stream):
+        return _fp8_prepare_alloc(q, k, v, hadamard_signs, per_tensor, cu_seqlens, max_seqlen, rope_cos, rope_sin,
+                                  stream)
+
+
+def _fp8_prepare_alloc(q, k, v, hadamard_signs, per_tensor, cu_seqlens, max_seqlen, rope_cos, rope_sin, stream):
     if cu_seqlens is None:
         B, N, Hq, d = q.shape
         Hkv = k.shape[2]
