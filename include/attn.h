@@ -71,7 +71,9 @@ enum {
  * Variable-length layout (cu_seqlens != NULL; sequences packed along one token axis, the
  * varlen interface of the guijiagi overview's "variable-length sequences" paragraph):
  *   cu_seqlens: int32 [B + 1] on the device, cu_seqlens[0] = 0, non-decreasing; sequence b
- *   holds tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 and T = cu_seqlens[B].
+ *   holds tokens cu_seqlens[b] .. cu_seqlens[b+1]-1 and T = cu_seqlens[B].  The offsets are
+ *   read on the device only, so the library cannot validate them: offsets that decrease or
+ *   pass the T tokens the tensors hold make the kernels access memory outside the tensors.
  *   q, o  [T, Hq, d]        k, v [T, Hkv, d]        lse [Hq, T]
  *   N must be >= the longest sequence (it sizes the grid, so no device-to-host copy is
  *   needed; the library cannot check it without one).  A longer sequence is treated as its
