@@ -29,7 +29,7 @@ import re
 
 import torch
 
-__all__ = ["AttnError", "attn_fwd", "attn_fwd_window", "attn_bwd", "attn_bwd_window", "attn_bwd_noalloc",
+__all__ = ["AttnError", "check_cu_seqlens", "attn_fwd", "attn_fwd_window", "attn_bwd", "attn_bwd_window", "attn_bwd_noalloc",
            "attention_backward", "attn_fp8_prepare", "attn_fp8_prepare_ex", "attn_strerror", "attention",
            "fp8_prepare", "load_library", "LIB_PATH", "ATTN_BF16", "ATTN_FP16", "ATTN_FP8_E4M3",
            "ATTN_FP8_SCALE_BLOCK", "ATTN_FP8_SCALE_TENSOR"]
@@ -242,6 +242,30 @@ def attn_fwd_window(q, k, v, o, lse, *, window: int, alpha: float | None = None,
         st = lib.attn_fwd_window(*head, int(window), *tail, _stream_handle(stream, dev))
     if st != ATTN_OK:
         raise AttnError(st, "attn_fwd_window")
+
+
+def check_cu_seqlens(cu_seqlens, total_tokens: int, max_seqlen: int | None = None) -> None:
+    """Validate packed-layout offsets on the host before a call.  The library reads them on the
+    device only and cannot check them; offsets that decrease or pass the tensors' tokens make
+    its kernels access memory outside the tensors.  This copies them to the host, so it waits
+    for the work that writes them: meant for debugging and input pipelines, not for every call.
+    Raises ValueError unless cu_seqlens is a 1-D int32 tensor of at least two entries that
+    starts at 0, never decreases and ends at ``total_tokens`` (the token count of q, k and v),
+    and, when ``max_seqlen`` is given, no sequence is longer than it."""
+    if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dim() != 1 or cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor")
+    cu = cu_seqlens.cpu().tolist()
+    if len(cu) < 2:
+        raise ValueError("cu_seqlens needs at least two entries (one sequence)")
+    if cu[0] != 0:
+        raise ValueError(f"cu_seqlens[0] must be 0, got {cu[0]}")
+    lengths = [b - a for a, b in zip(cu, cu[1:])]
+    if min(lengths) < 0:
+        raise ValueError(f"cu_seqlens decreases after entry {lengths.index(min(lengths))}")
+    if cu[-1] != int(total_tokens):
+        raise ValueError(f"cu_seqlens ends at {cu[-1]}, but the tensors hold {int(total_tokens)} tokens")
+    if max_seqlen is not None and max(lengths) > int(max_seqlen):
+        raise ValueError(f"a sequence of {max(lengths)} tokens is longer than max_seqlen = {int(max_seqlen)}")
 
 
 def attention(q, k, v, *, causal: bool = False, alpha: float | None = None, cu_seqlens=None,
