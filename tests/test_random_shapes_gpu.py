@@ -1,7 +1,7 @@
 """GPU parity on seeded random problem shapes: each case draws batch or packed sequence lengths,
 head counts (any grouping), head dim, mask (none, causal, causal sliding window) and 16-bit
-dtype, or the FP8 path with its pre-pass, and compares every element of O and L with the fp64
-oracle on the same inputs.  The hand-picked cases of the other test files cover each code path
+dtype, or the FP8 path with its pre-pass (block scales, or for every other FP8 draw one scale
+per tensor), and compares every element of O and L with the fp64 oracle on the same inputs.  The hand-picked cases of the other test files cover each code path
 on purpose; these cover combinations of them.  Sizes stay small (at most about 1000 tokens per
 sequence) so the oracle runs every row in seconds.
 
@@ -45,6 +45,12 @@ def _draw(case: int):
     return inp, fp8
 
 
+def _per_tensor(case: int) -> bool:
+    """FP8 draws alternate between block and per-tensor scales (by case index, so the seeded
+    draws themselves do not change)."""
+    return case % 8 == 7
+
+
 def _describe(inp, fp8):
     cu = None if inp.cu_seqlens is None else np.diff(inp.cu_seqlens).tolist()
     return (f"{'fp8' if fp8 else inp.dtype} B={inp.B} N={inp.N} Hq={inp.Hq} Hkv={inp.Hkv} d={inp.d} "
@@ -56,9 +62,9 @@ def _describe(inp, fp8):
 def test_random_shape(case):
     inp, fp8 = _draw(case)
     what = _describe(inp, fp8)
-    gu.say("random shape", case, what)
+    gu.say("random shape", case, what, "per-tensor scales" if fp8 and _per_tensor(case) else "")
     if fp8:
-        o, lse, prep = gpu_fp8_attention(inp, si.hadamard_signs(128, seed=55))
+        o, lse, prep = gpu_fp8_attention(inp, si.hadamard_signs(128, seed=55), per_tensor=_per_tensor(case))
         assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), "rows left unwritten"
         check_fp8(*_three_errors(inp, o, lse, prep, *_all_rows(inp)))
         return
@@ -109,6 +115,8 @@ def test_draws_cover_the_modes():
         seen.add(("fp8" if fp8 else inp.dtype, inp.d, "window" if inp.window else ("causal" if inp.causal else "none"),
                   inp.cu_seqlens is not None))
     assert {k[0] for k in seen} == {"bf16", "fp16", "fp8"}
+    fp8_cases = [c for c in range(N_CASES) if _draw(c)[1]]
+    assert {_per_tensor(c) for c in fp8_cases} == {False, True}, "FP8 draws must use both scalings"
     assert {k[1] for k in seen} == {64, 128, 256}
     assert {k[2] for k in seen} == {"none", "causal", "window"}
     assert {k[3] for k in seen} == {False, True}
