@@ -97,6 +97,18 @@ def test_bwd_varlen(causal):
     check_grads(inp, do, run_gpu_bwd(inp, do), f"bwd packed causal={causal}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Hq,Hkv,d", [(5, 5, 64), (7, 1, 128), (14, 7, 64), (3, 3, 128)])
+def test_bwd_odd_head_counts(Hq, Hkv, d, causal):
+    """Head counts that do not split evenly over the eight XCDs; dense and packed."""
+    inp = si.dense_inputs(2, 217, Hq, d, Hkv=Hkv, causal=causal, seed=950 + Hq + Hkv + d)
+    do = si.output_gradient(inp, 5)
+    check_grads(inp, do, run_gpu_bwd(inp, do), f"bwd odd heads Hq={Hq} Hkv={Hkv} d={d} causal={causal}")
+    inp = si.varlen_inputs([217, 0, 64, 300], Hq, Hkv, d, causal=causal, seed=960 + Hq + Hkv + d)
+    do = si.output_gradient(inp, 6)
+    check_grads(inp, do, run_gpu_bwd(inp, do), f"bwd odd heads packed Hq={Hq} Hkv={Hkv} d={d} causal={causal}")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_bwd_full_size(d):
     """B=1, N=4096, 16 heads, causal; the oracle checks two heads."""

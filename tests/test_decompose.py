@@ -121,7 +121,8 @@ def test_workload_grids(harness, name, lengths, Hq, Hkv, br, causal):
 
 # head splits of every branch: KV groups of 1 and 3 heads on one XCD, one query head at a time
 # (Hkv not a multiple of 8), and the contiguous-range fallback (Hq not a multiple of 8)
-SPLITS = [(8, 8), (24, 8), (16, 4), (8, 1), (8, 2), (12, 4), (2, 2), (6, 3), (40, 8), (64, 16)]
+SPLITS = [(8, 8), (24, 8), (16, 4), (8, 1), (8, 2), (12, 4), (2, 2), (6, 3), (40, 8), (64, 16),
+          (1, 1), (3, 1), (5, 5), (7, 1), (10, 2), (14, 7)]
 
 
 @pytest.mark.parametrize("causal", [False, True])

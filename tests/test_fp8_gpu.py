@@ -325,6 +325,20 @@ def test_fp8_attention_dense_gqa(causal):
     check_fp8(*_three_errors(inp, o, lse, prep, *_all_rows(inp)))
 
 
+@pytest.mark.parametrize("packed", [False, True])
+@pytest.mark.parametrize("Hq,Hkv", [(5, 5), (7, 1), (14, 7)])
+def test_fp8_attention_odd_heads(Hq, Hkv, packed):
+    """Head counts that do not split evenly over the eight XCDs, causal, every row checked."""
+    if packed:
+        inp = si.varlen_inputs([333, 0, 95, 512], Hq, Hkv, 128, causal=True, seed=620 + Hq)
+    else:
+        inp = si.dense_inputs(2, 333, Hq, 128, Hkv=Hkv, causal=True, seed=630 + Hq)
+    gu.say("fp8 attention odd heads", Hq, Hkv, packed)
+    o, lse, prep = gpu_fp8_attention(inp, si.hadamard_signs(128, seed=55))
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    check_fp8(*_three_errors(inp, o, lse, prep, *_all_rows(inp)))
+
+
 @pytest.mark.parametrize("per_tensor", [False, True])
 @pytest.mark.parametrize("causal", [True, False])
 def test_fp8_attention_varlen(causal, per_tensor):

@@ -145,6 +145,21 @@ def test_varlen_head_splits(Hq, Hkv):
     _compare_full(inp, f"varlen head split Hq={Hq} Hkv={Hkv}")
 
 
+ODD_HEADS = [(1, 1, 128), (3, 1, 64), (5, 5, 128), (7, 1, 256), (10, 2, 128), (14, 7, 64)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Hq,Hkv,d", ODD_HEADS)
+def test_odd_head_counts(Hq, Hkv, d, causal):
+    """Head counts that do not split evenly over the eight XCDs: one head, primes, groups of
+    five and seven query heads per KV head; dense and packed."""
+    seed = 900 + Hq + 3 * Hkv + d + causal
+    inp = si.dense_inputs(2, 333, Hq, d, Hkv=Hkv, causal=causal, seed=seed)
+    _compare_full(inp, f"odd heads Hq={Hq} Hkv={Hkv} d={d} causal={causal}")
+    inp = si.varlen_inputs([333, 0, 95, 512], Hq, Hkv, d, causal=causal, seed=seed + 1)
+    _compare_full(inp, f"odd heads packed Hq={Hq} Hkv={Hkv} d={d} causal={causal}")
+
+
 def test_varlen_max_seqlen_above_longest():
     """N larger than every sequence only grows the grid; extra blocks exit."""
     inp = si.varlen_inputs([5, 130], 2, 2, 128, causal=True, seed=300)
