@@ -98,6 +98,16 @@ def test_bwd_varlen(causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,N", [(300, 1), (97, 3), (33, 65)])
+def test_bwd_tiny_sequences(B, N, d, causal):
+    """Large batches of sequences shorter than one tile (or one key past it)."""
+    inp = si.dense_inputs(B, N, 4, d, Hkv=2, causal=causal, seed=970 + B + N + d + causal)
+    do = si.output_gradient(inp, 7)
+    check_grads(inp, do, run_gpu_bwd(inp, do), f"bwd tiny sequences B={B} N={N} d={d} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("Hq,Hkv,d", [(5, 5, 64), (7, 1, 128), (14, 7, 64), (3, 3, 128)])
 def test_bwd_odd_head_counts(Hq, Hkv, d, causal):
     """Head counts that do not split evenly over the eight XCDs; dense and packed."""

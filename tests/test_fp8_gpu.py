@@ -325,6 +325,17 @@ def test_fp8_attention_dense_gqa(causal):
     check_fp8(*_three_errors(inp, o, lse, prep, *_all_rows(inp)))
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,N", [(300, 1), (97, 3), (33, 65)])
+def test_fp8_attention_tiny_sequences(B, N, causal):
+    """Large batches of sequences shorter than one block (or one token past it), every row."""
+    inp = si.dense_inputs(B, N, 4, 128, Hkv=2, causal=causal, seed=640 + B + N + causal)
+    gu.say("fp8 attention tiny sequences", B, N, causal)
+    o, lse, prep = gpu_fp8_attention(inp, si.hadamard_signs(128, seed=55))
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    check_fp8(*_three_errors(inp, o, lse, prep, *_all_rows(inp)))
+
+
 @pytest.mark.parametrize("packed", [False, True])
 @pytest.mark.parametrize("Hq,Hkv", [(5, 5), (7, 1), (14, 7)])
 def test_fp8_attention_odd_heads(Hq, Hkv, packed):

@@ -160,6 +160,16 @@ def test_odd_head_counts(Hq, Hkv, d, causal):
     _compare_full(inp, f"odd heads packed Hq={Hq} Hkv={Hkv} d={d} causal={causal}")
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("B,N", [(300, 1), (97, 3), (33, 65)])
+def test_many_tiny_sequences(B, N, d, causal):
+    """Large batches of sequences shorter than one tile (or one key past it): every block is a
+    ragged tail."""
+    inp = si.dense_inputs(B, N, 4, d, Hkv=2, causal=causal, seed=1000 + B + N + d + causal)
+    _compare_full(inp, f"tiny sequences B={B} N={N} d={d} causal={causal}")
+
+
 def test_varlen_max_seqlen_above_longest():
     """N larger than every sequence only grows the grid; extra blocks exit."""
     inp = si.varlen_inputs([5, 130], 2, 2, 128, causal=True, seed=300)
