@@ -5,7 +5,9 @@ attn_fwd addresses one head's K/V rows with 32-bit byte offsets and accepts N * 
 every head dim runs causal attention with N = 131071 and Hkv chosen so that a head's K/V rows
 span just under 2 GiB: the last tiles sit at the top of the offset range.  The inputs (2.1 GB per
 tensor) come from a seeded generator on the device; the oracle gets the K/V columns of the
-sampled heads only and checks sampled rows, among them the first and the last tokens.
+sampled heads only and checks sampled rows, among them the first and the last tokens.  The FP8
+path has its own limit (N * Hkv * d bytes of e4m3 codes per tensor below 2^31) and its own case
+just under it.
 """
 import numpy as np
 import pytest
@@ -53,4 +55,53 @@ def test_largest_kv_span(d, H):
     gu.say("largest K/V span", m)
     gu.check(m, what=f"N={N} H={H} d={d}")
     del q, k, v, o, lse
+    torch.cuda.empty_cache()
+
+
+def test_fp8_largest_span():
+    """FP8 attention accepts N * Hkv * d up to 2^31 - 1 bytes of e4m3 codes per tensor: causal,
+    N = 131071, H = 128, d = 128 sits just under it.  The pre-pass and the attention run on the
+    device; sampled rows of three heads are checked against fp64 on the bf16 inputs (the 3e-2
+    bar) and against exact attention on the kernel's own dequantised inputs (its own-error
+    bounds), with only those heads' columns copied to the host."""
+    import exact_attention_76_amd as ea
+    import seeded_inputs as si
+    from oracle import fp8 as ofp8
+    from tests.test_fp8_gpu import _own, check_own
+
+    H, d = 128, 128
+    assert N * H * d <= 2**31 - 1 and N * H * d > 2**31 - 2**15
+    gu.say("fp8 largest span", f"N={N} H={H} d={d}")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(950)
+    q, k, v = (torch.randn((1, N, H, d), generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+               for _ in range(3))
+    signs = torch.from_numpy(si.hadamard_signs(128, seed=55)).cuda()
+    q8, k8, v8, qs, ks, vs = ea.fp8_prepare(q, k, v, hadamard_signs=signs)
+    alpha = d ** -0.5
+    o, lse = ea.attention(q8, k8, v8, causal=True, alpha=alpha, q_scale=qs, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(lse).all()), "non-finite LSE"
+
+    heads = np.array([0, H // 2, H - 1])
+    rng = np.random.default_rng(951)
+    tokens = np.concatenate([np.array([0, 1, 63, 64, N // 2, N - 65, N - 2, N - 1]), rng.integers(0, N, 8)])
+    rows_h = np.repeat(np.arange(len(heads)), len(tokens))
+    rows_t = np.tile(tokens, len(heads))
+    sub = lambda t: t[:, :, heads, :].contiguous()
+    qf, kf, vf = (_bits_to_f64(sub(t)) for t in (q, k, v))
+    codes = [sub(t).cpu().numpy() for t in (q8, k8, v8)]
+    scales = [t[:, heads, :].contiguous().cpu().numpy() for t in (qs, ks, vs)]
+    qd, kd, vd = (ofp8.dequantize(c, s) for c, s in zip(codes, scales))
+    o_ref, lse_ref = oracle.attention_rows(qf, kf, vf, rows_h, rows_t, causal=True, alpha=alpha)
+    o_dq, lse_dq = oracle.attention_rows(qd, kd, vd, rows_h, rows_t, causal=True, alpha=alpha)
+    o_got = o[0, rows_t, heads[rows_h]].double().cpu().numpy()
+    lse_got = lse[0, heads[rows_h], rows_t].double().cpu().numpy()
+    X = oracle.error_metrics(o_got, o_ref, lse_got, lse_ref)
+    gu.say("fp8 largest span vs fp64", X)
+    assert X["rmse"] <= gu.TOL_FP8_RMSE, X
+    view = si.AttnInputs(None, None, None, "bf16", 1, N, len(heads), len(heads), d, True)
+    Z, own = _own(view, o_got, lse_got, o_dq, lse_dq, (qd, kd, vd), rows_h, rows_t, True)
+    check_own(Z, own)
+    del q, k, v, q8, k8, v8, o, lse
     torch.cuda.empty_cache()
